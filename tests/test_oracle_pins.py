@@ -1,0 +1,352 @@
+"""Pins for the CPU oracle, checked against things other than itself:
+hand-worked fixtures (tests/golden), library routines (numpy float16),
+exact rational brute force, closed forms, invariants and symmetries.
+
+Pages: "BitCPM ternary (1.58-bit)" (TQ2_0 format, pack rule, block
+decomposition, exact round trip) and "gemma4 wNa8o8 requires int8
+activations" (static int8 quantizer).
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from ternary_packed_weight_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _lines(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if line:
+                out.append(line)
+    return out
+
+
+def _ternary_W(q, d):
+    """W = d_b * (q - 1) in fp32 (test-side construction of a ternary weight)."""
+    N, K = q.shape
+    dd = np.repeat(d.astype(np.float32), 256, axis=1)
+    return (dd * (q.astype(np.float32) - 1.0)).astype(np.float32)
+
+
+def _fields_to_bytes(q):
+    """Test-side statement of the byte layout: element k at bits 2*(k%4)."""
+    q = q.astype(np.uint8)
+    return (q[:, 0::4] | (q[:, 1::4] << 2) | (q[:, 2::4] << 4) | (q[:, 3::4] << 6)).astype(np.uint8)
+
+
+# ---------------------------------------------------------------- binary16
+
+def test_half_to_float_matches_numpy_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.half_to_float(int(b)) for b in bits], np.float32)
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite].view(np.uint32), ref[finite].view(np.uint32))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+
+
+def test_float_to_half_golden():
+    for line in _lines("fp16_scale_rounding.txt"):
+        v, b = line.split()[:2]
+        assert oracle.float_to_half(float(np.float32(float(v)))) == int(b, 16), line
+
+
+def test_float_to_half_matches_numpy_random():
+    g = np.random.Generator(np.random.PCG64(7))
+    mags = np.concatenate([
+        g.uniform(0, 1, 20000), g.uniform(0, 70000, 5000),
+        np.exp(g.uniform(-20, 0, 10000)) * 1e-3,
+        g.uniform(0.005, 0.05, 5000),
+    ]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        ref = mags.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.float_to_half(float(v)) for v in mags], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- pack
+
+def test_pack_golden_exact_block():
+    lines = _lines("pack_exact_block.txt")
+    scale = int(lines[2].split()[1], 16)
+    expect = bytes.fromhex(lines[3].split()[1])
+    k = np.arange(256)
+    W = (np.float32(0.75) * ((k % 3).astype(np.float32) - 1)).astype(np.float32)[None, :]
+    codes, scales, bad = oracle.pack(W)
+    assert bad == 0
+    assert scales[0, 0] == scale
+    assert codes.tobytes() == expect
+
+
+def test_pack_golden_rounding_block():
+    lines = _lines("pack_rounding_block.txt")
+    scale = int(lines[1].split()[1], 16)
+    vals = [float(v) for v in lines[2].split()[1:]]
+    W = np.zeros((1, 256), np.float32)
+    W[0, :len(vals)] = np.array(vals, np.float32)
+    codes, scales, bad = oracle.pack(W)
+    assert bad == 0
+    assert scales[0, 0] == scale
+    assert codes[0, 0] == 0x26 and codes[0, 1] == 0x25
+    assert np.all(codes[0, 2:] == 0x55)
+
+
+@pytest.mark.parametrize("N,K,seed", [(3, 256, 1), (17, 768, 2), (64, 4096, 3)])
+def test_pack_round_trip_exact(N, K, seed):
+    """Page claim: d_block = max|W| is exact and the pack/dequant round trip
+    has max error 0 for a weight of ternary form."""
+    q, d, _ = synth.problem(seed, N, K)
+    W = _ternary_W(q, d)
+    codes, scales, bad = oracle.pack(W)
+    assert bad == 0
+    assert np.array_equal(scales, synth.bits(d).reshape(N, K // 256))
+    assert np.array_equal(codes, _fields_to_bytes(q))
+    W2 = oracle.dequant(codes, scales, N, K)
+    assert np.max(np.abs(W2 - W)) == 0.0
+    assert np.array_equal(W2.view(np.uint32) & 0x7FFFFFFF, W.view(np.uint32) & 0x7FFFFFFF)
+
+
+def test_pack_generic_weight_properties():
+    """For a non-ternary W: d is fp16(max|W|), |W - d(q-1)| <= d/2 (+fp32
+    division slack), codes in {0,1,2}, and the sign of a nonzero code
+    matches the sign of W."""
+    g = synth.rng(11)
+    W = synth.dense_weight(g, 9, 1024)
+    codes, scales, bad = oracle.pack(W)
+    assert bad == 0
+    q = np.stack([(codes >> (2 * j)) & 3 for j in range(4)], axis=-1).reshape(9, 1024)
+    assert q.max() <= 2
+    d = scales.view(np.float16).astype(np.float64)
+    blockmax = np.abs(W.reshape(9, 4, 256)).max(axis=2)
+    assert np.array_equal(scales, blockmax.astype(np.float32).astype(np.float16).view(np.uint16))
+    dd = np.repeat(d, 256, axis=1)
+    err = np.abs(W - dd * (q.astype(np.float64) - 1))
+    assert np.all(err <= dd * 0.5 * (1 + 1e-6) + 1e-12)
+    nz = q != 1
+    assert np.all(np.sign(W[nz]) == (q[nz].astype(np.int64) - 1))
+
+
+def test_pack_zero_block_and_bad_blocks():
+    W = np.zeros((2, 512), np.float32)
+    W[1, 256:] = 1.0
+    W[1, 300] = np.inf
+    codes, scales, bad = oracle.pack(W)
+    assert bad == 1
+    assert scales[0, 0] == 0 and scales[0, 1] == 0 and scales[1, 0] == 0
+    assert np.all(codes[0] == 0x55) and np.all(codes[1, :64] == 0x55)
+    W = np.full((1, 256), 70000.0, np.float32)
+    _, _, bad = oracle.pack(W)
+    assert bad == 1
+
+
+# ---------------------------------------------------------------- gemv
+
+def _gemv_from_q(q, d_bits, x_bits):
+    N, K = q.shape
+    codes = _fields_to_bytes(q)
+    return oracle.gemv(codes, d_bits.reshape(N, K // 256), N, K, x_bits)
+
+
+def test_gemv_golden_small():
+    lines = _lines("gemv_small.txt")
+    yA = [float(v) for v in lines[0].split()[2:]]
+    k = np.arange(256)
+    x = (0.25 * (k % 8)).astype(np.float16)
+    q = np.stack([np.full(256, 2), np.where(k % 2 == 0, 0, 2), np.full(256, 1)]).astype(np.uint8)
+    d = np.array([[1.0], [0.5], [0.75]], np.float16)
+    y = _gemv_from_q(q, synth.bits(d), synth.bits(x))
+    assert list(y) == yA
+    yB = float(lines[2].split()[2])
+    qB = np.full((1, 512), 2, np.uint8)
+    dB = np.array([[1.0, 2.0]], np.float16)
+    y = _gemv_from_q(qB, synth.bits(dB), synth.bits(np.ones(512, np.float16)))
+    assert y[0] == yB
+
+
+@pytest.mark.parametrize("N,K,seed", [(1, 256, 21), (3, 256, 22), (5, 512, 23), (2, 512, 24)])
+def test_gemv_brute_force(N, K, seed):
+    """Oracle fp64 sum vs the exact rational sum: error within fp64 summation
+    error plus one fp32 rounding."""
+    q, d, x = synth.problem(seed, N, K, outliers=(seed % 2 == 0))
+    y = _gemv_from_q(q, synth.bits(d), synth.bits(x))
+    exact = brute.exact_gemv(q, synth.bits(d), synth.bits(x))
+    l1 = brute.exact_l1(q, synth.bits(d), synth.bits(x))
+    for n in range(N):
+        e64 = Fraction(K * 2.0 ** -52) * l1[n]
+        ulp32 = Fraction(float(np.spacing(np.float32(abs(float(exact[n])) + float(e64)))))
+        assert abs(Fraction(float(y[n])) - exact[n]) <= ulp32 / 2 + e64 + Fraction(1, 2 ** 149), n
+
+
+def test_block_decomposition_identity():
+    """Page identity: sum_k x_k d_b (q_k-1) = sum_b d_b sum_{k in b} x_k (q_k-1)."""
+    q, d, x = synth.problem(31, 3, 768)
+    a = brute.exact_gemv(q, synth.bits(d), synth.bits(x))
+    b = brute.exact_gemv_blockwise(q, synth.bits(d), synth.bits(x))
+    assert a == b
+    y = _gemv_from_q(q, synth.bits(d), synth.bits(x))
+    for n in range(3):
+        assert abs(float(y[n]) - float(b[n])) <= 1e-6 * float(brute.exact_l1(q, synth.bits(d), synth.bits(x))[n])
+
+
+def test_one_hot_columns_pin_field_order():
+    """x = e_k for every k of two blocks: y_n = d_{n,b}(q_{n,k}-1) exactly, on
+    both paths.  Pins every bit position of the layout."""
+    N, K = 5, 512
+    q, d, _ = synth.problem(41, N, K)
+    codes = _fields_to_bytes(q)
+    scales = synth.bits(d).reshape(N, K // 256)
+    df = d.astype(np.float32)
+    for k in range(K):
+        x = np.zeros(K, np.float16)
+        x[k] = 1.0
+        y = oracle.gemv(codes, scales, N, K, synth.bits(x))
+        expect = df[:, k // 256] * (q[:, k].astype(np.float32) - 1)
+        assert np.array_equal(y, expect), k
+        xq = oracle.quantize_i8(synth.bits(x), np.float32(0.01))
+        assert xq[k] == 100 and np.count_nonzero(xq) == 1
+        yi, P = oracle.gemv_i8q(codes, scales, N, K, xq, np.float32(0.01))
+        assert np.array_equal(P[:, k // 256], 100 * (q[:, k].astype(np.int32) - 1))
+        ref = brute.exact_i8_y(q, synth.bits(d), xq, np.float32(0.01))
+        assert np.array_equal(yi, ref)
+
+
+def test_special_cases():
+    N, K = 4, 1024
+    g = synth.rng(51)
+    x = synth.activations(g, K)
+    xb = synth.bits(x)
+    d = synth.scales(g, N, K)
+    # all codes 1 -> y == 0 exactly
+    y = _gemv_from_q(np.ones((N, K), np.uint8), synth.bits(d), xb)
+    assert np.all(y == 0)
+    # all codes 2 with d = 1 -> y = sum x (fsum is the exact sum rounded once)
+    one = np.ones((N, K // 256), np.float16)
+    y = _gemv_from_q(np.full((N, K), 2, np.uint8), synth.bits(one), xb)
+    ref = np.float32(math.fsum(x.astype(np.float64)))
+    assert np.all(y == ref)
+    # all codes 0 -> y = -d * sum x with one d for the row
+    y0 = _gemv_from_q(np.zeros((N, K), np.uint8), synth.bits(one), xb)
+    assert np.all(y0 == -ref)
+    # identity: N = K = 256, code 2 on the diagonal, 1 elsewhere -> y = d x
+    q = np.ones((256, 256), np.uint8)
+    np.fill_diagonal(q, 2)
+    dI = np.full((256, 1), 0.75, np.float16)
+    xs = x[:256]
+    y = _gemv_from_q(q, synth.bits(dI), synth.bits(xs))
+    assert np.array_equal(y, (np.float32(0.75) * xs.astype(np.float32)))
+
+
+def test_symmetries():
+    N, K = 6, 1024
+    q, d, x = synth.problem(61, N, K)
+    xb = synth.bits(x)
+    y = _gemv_from_q(q, synth.bits(d), xb)
+    # q -> 2 - q negates y exactly
+    yneg = _gemv_from_q((2 - q).astype(np.uint8), synth.bits(d), xb)
+    assert np.array_equal(yneg, -y)
+    # doubling every d doubles y exactly
+    y2 = _gemv_from_q(q, synth.bits((d.astype(np.float32) * 2).astype(np.float16)), xb)
+    assert np.array_equal(y2, 2 * y)
+    # permuting rows permutes y
+    perm = synth.rng(62).permutation(N)
+    yp = _gemv_from_q(q[perm], synth.bits(d)[perm], xb)
+    assert np.array_equal(yp, y[perm])
+    # int8 path: negation is exact too
+    s = np.float32(np.abs(x.astype(np.float32)).max() / np.float32(100))
+    codes = _fields_to_bytes(q)
+    codesn = _fields_to_bytes((2 - q).astype(np.uint8))
+    sc = synth.bits(d).reshape(N, K // 256)
+    yi = oracle.gemv_i8(codes, sc, N, K, xb, s)
+    yin = oracle.gemv_i8(codesn, sc, N, K, xb, s)
+    assert np.array_equal(yin, -yi)
+
+
+# ---------------------------------------------------------------- int8
+
+def test_quantize_golden():
+    for line in _lines("quantize_i8.txt"):
+        s, x, e = line.split()[:3]
+        xb = synth.bits(np.array([float(x)], np.float16))
+        assert np.float16(float(x)).astype(np.float64) == float(x), line
+        got = oracle.quantize_i8(xb, np.float32(float(s)))
+        assert int(got[0]) == int(e), line
+
+
+def test_quantize_integer_case_and_clip_count():
+    g = synth.rng(71)
+    xi = g.integers(-128, 128, size=4096).astype(np.float16)
+    assert np.array_equal(oracle.quantize_i8(synth.bits(xi), np.float32(1.0)), xi.astype(np.int8))
+    x = synth.activations(g, 4096)
+    amax = np.float32(np.abs(x.astype(np.float32)).max())
+    s = np.float32(amax / np.float32(200))
+    xq = oracle.quantize_i8(synth.bits(x), s)
+    v = x.astype(np.float64) / float(s)
+    # top code 127 <=> quotient above 126.5 (127.5 ties to 128, clamped);
+    # bottom code -128 <=> quotient at or below -127.5 (ties to -128)
+    assert np.count_nonzero(v >= 127.5) > 0 and np.count_nonzero(v <= -127.5) > 0
+    assert np.count_nonzero(xq == 127) == np.count_nonzero(v > 126.5)
+    assert np.count_nonzero(xq == -128) == np.count_nonzero(v <= -127.5)
+    # monotone and within half a step where not clipped
+    order = np.argsort(x.astype(np.float32), kind="stable")
+    assert np.all(np.diff(xq[order].astype(np.int32)) >= 0)
+    inside = (xq > -128) & (xq < 127)
+    err = np.abs(xq[inside].astype(np.float64) * float(s) - x[inside].astype(np.float64))
+    assert np.all(err <= float(s) * (0.5 + 1e-6))
+
+
+def test_int8_golden_small():
+    lines = _lines("gemv_small.txt")
+    PA = [int(v) for v in lines[1].split()[2:]]
+    k = np.arange(256)
+    x = (0.25 * (k % 8)).astype(np.float16)
+    q = np.stack([np.full(256, 2), np.where(k % 2 == 0, 0, 2), np.full(256, 1)]).astype(np.uint8)
+    d = np.array([[1.0], [0.5], [0.75]], np.float16)
+    codes = _fields_to_bytes(q)
+    xq = oracle.quantize_i8(synth.bits(x), np.float32(0.25))
+    assert np.array_equal(xq, (k % 8).astype(np.int8))
+    y, P = oracle.gemv_i8q(codes, synth.bits(d), 3, 256, xq, np.float32(0.25))
+    assert list(P[:, 0]) == PA
+    assert list(y) == [float(v) for v in lines[0].split()[2:]]
+    qB = np.full((1, 512), 2, np.uint8)
+    dB = np.array([[1.0, 2.0]], np.float16)
+    yB = oracle.gemv_i8(_fields_to_bytes(qB), synth.bits(dB), 1, 512,
+                        synth.bits(np.ones(512, np.float16)), np.float32(1 / 64))
+    assert yB[0] == float(lines[2].split()[2])
+    xqB = oracle.quantize_i8(synth.bits(np.ones(512, np.float16)), np.float32(1 / 64))
+    _, PB = oracle.gemv_i8q(_fields_to_bytes(qB), synth.bits(dB), 1, 512, xqB, np.float32(1 / 64))
+    assert list(PB[0]) == [int(v) for v in lines[3].split()[2:]]
+
+
+@pytest.mark.parametrize("N,K,seed,div", [(3, 256, 81, 100), (4, 512, 82, 200), (2, 768, 83, 100)])
+def test_int8_brute_force(N, K, seed, div):
+    q, d, x = synth.problem(seed, N, K, outliers=(div == 200))
+    s = np.float32(np.float32(np.abs(x.astype(np.float32)).max()) / np.float32(div))
+    xq = oracle.quantize_i8(synth.bits(x), s)
+    codes = _fields_to_bytes(q)
+    sc = synth.bits(d).reshape(N, K // 256)
+    y, P = oracle.gemv_i8q(codes, sc, N, K, xq, s)
+    assert P.tolist() == brute.exact_partials(q, xq)
+    assert np.array_equal(oracle.partials_i8(codes, N, K, xq), P)
+    assert np.array_equal(y, brute.exact_i8_y(q, synth.bits(d), xq, s))
+    assert np.array_equal(oracle.gemv_i8(codes, sc, N, K, synth.bits(x), s), y)
+
+
+def test_int8_large_scales_exact():
+    """Scales near the top of binary16 exercise the full D = d*2^24 range."""
+    N, K = 2, 512
+    q, _, x = synth.problem(91, N, K)
+    d = np.array([[65504.0, 2.0 ** -24], [1000.0, 6.1e-5]], np.float16)
+    s = np.float32(0.03)
+    xq = oracle.quantize_i8(synth.bits(x), s)
+    y, _ = oracle.gemv_i8q(_fields_to_bytes(q), synth.bits(d), N, K, xq, s)
+    assert np.array_equal(y, brute.exact_i8_y(q, synth.bits(d), xq, s))
