@@ -1,0 +1,159 @@
+/*
+ * tq2.h -- C ABI of libtq2, the TQ2_0 ternary decode matvec for MI355X
+ * (gfx950).
+ *
+ * The method (page "BitCPM ternary (1.58-bit)", TQ2_0 paragraph): a weight
+ * W[N][K] is stored in blocks of 256 consecutive elements along K; every
+ * element is a 2-bit code q in {0,1,2} standing for q-1 in {-1,0,+1}, and
+ * every block carries one fp16 scale d, so W[n][k] = d[n][k/256]*(q[n][k]-1).
+ * The matvec y = W x is computed per block, sum_b d_b * sum_{k in b} x_k(q_k-1)
+ * (same page, kernel paragraph).
+ *
+ * Byte layout (our own; the pages fix no interleave):
+ *   codes  : uint8  [N][K/4], row-major.  Element k of row n is in byte
+ *            n*(K/4) + k/4 at bits 2*(k%4) and 2*(k%4)+1, least significant
+ *            first.  One block = 64 bytes, one 16-byte word = 64 elements.
+ *   scales : uint16 [N][K/256], row-major, IEEE binary16 bit patterns.
+ * Codes and scales live in two separate planes so that every code row is
+ * 16-byte aligned.  Bytes per block: 64 + 2.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers that the caller allocates, owns
+ *     and keeps alive until the work completes.  The library allocates
+ *     nothing and keeps no mutable state; calls are thread-safe.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     default stream) and returns; results are valid once the caller has
+ *     synchronized the stream.  Nothing synchronizes inside.
+ *   - Arguments are validated before anything is launched; on error nothing
+ *     is written and a TQ2_ERR_* status is returned.  Shapes are never padded
+ *     or truncated.  Device faults surface at the caller's synchronization.
+ *   - Outputs must not alias inputs.
+ *   - K must be a positive multiple of 256 and at most TQ2_MAX_K
+ *     (TQ2_I8_MAX_K on the int8 path).  N is any value >= 1, N*K < 2^40.
+ *   - Alignment: codes, x, x_q and W 16 bytes; scales 2; y, partials 4;
+ *     workspace 256.
+ */
+#ifndef TQ2_H
+#define TQ2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ2_ABI_VERSION 1
+#define TQ2_BLOCK 256
+#define TQ2_MAX_K 65536    /* fp16 activations staged on chip: 16 x 4096 */
+#define TQ2_I8_MAX_K 65280 /* 255 blocks: keeps the exact int64 sum in range */
+
+enum tq2_status {
+    TQ2_OK = 0,
+    TQ2_ERR_ARG = 1,       /* null pointer, N < 1, unknown op, aliasing    */
+    TQ2_ERR_SHAPE = 2,     /* K < 256, K % 256 != 0, K too large           */
+    TQ2_ERR_ALIGN = 3,     /* a pointer violates its alignment             */
+    TQ2_ERR_WORKSPACE = 4, /* workspace missing or smaller than required   */
+    TQ2_ERR_SCALE = 5,     /* int8 activation scale not finite or <= 0     */
+    TQ2_ERR_HIP = 6        /* the HIP runtime refused a launch             */
+};
+
+enum tq2_op {
+    TQ2_OP_GEMV = 0,
+    TQ2_OP_GATE_UP = 1,
+    TQ2_OP_GEMV_I8 = 2,
+    TQ2_OP_GEMV_I8Q = 3
+};
+
+typedef void *tq2_stream_t; /* hipStream_t */
+
+/* Version of this header the library was built from (TQ2_ABI_VERSION). */
+int32_t tq2_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *tq2_status_string(int32_t status);
+
+/* Sizes in bytes of the code plane (N*K/4) and the scale plane
+ * (N*(K/256)*2).  Return 0 for an invalid shape. */
+size_t tq2_codes_bytes(int64_t N, int64_t K);
+size_t tq2_scales_bytes(int64_t N, int64_t K);
+
+/* Device workspace an operation needs, in bytes (0 = none; pass NULL).
+ * `op` is a tq2_op; for TQ2_OP_GATE_UP, N is the row count of one matrix.  Returns (size_t)-1 for an invalid op or shape. */
+size_t tq2_workspace_bytes(int32_t op, int64_t N, int64_t K);
+
+/* tq2_pack -- fp32 W[N][K] (row-major) -> codes + scales.
+ * Page "BitCPM ternary (1.58-bit)", recovery paragraph: d_block = max|W|
+ * over the block, code = round(W/d) + 1.  Precisely: d is max|W| rounded to
+ * binary16 (nearest, ties to even); each code is rint(W/d) (IEEE fp32
+ * division by that rounded d, ties to even) clamped to [-1,1], plus 1; a
+ * block whose d is 0 gets code 1 everywhere.  For W of exact ternary form
+ * d*(q-1) the round trip is exact.
+ * bad_blocks (nullable, device int32): receives the number of blocks that
+ * hold a non-finite value or whose maximum rounds to binary16 infinity; the
+ * bytes written for such blocks are unspecified.
+ * Enqueues two kernels (counter reset, pack). */
+int32_t tq2_pack(const float *W, int64_t N, int64_t K, uint8_t *codes,
+                 uint16_t *scales, int32_t *bad_blocks, tq2_stream_t stream);
+
+/* tq2_dequant -- codes + scales -> fp32 W[N][K] = d*(q-1), exact.  A test
+ * aid; code 3 (never produced by tq2_pack) decodes as +2*d. */
+int32_t tq2_dequant(const uint8_t *codes, const uint16_t *scales, int64_t N,
+                    int64_t K, float *W, tq2_stream_t stream);
+
+/* tq2_gemv -- y[N] = W x with fp16 activations x[K] (binary16 bit
+ * patterns) and fp32 output.  Page "BitCPM ternary (1.58-bit)", kernel
+ * paragraph (block decomposition; per-lane partial times its block's d,
+ * then a cross-lane reduction); page "Custom Metal kernels" (tensors cross
+ * the kernel boundary in their native dtype, accumulation is fp32 in
+ * registers).  Accuracy: |y - y_exact| <= 2e-3 * sum_k |d_b(k) x_k| + 1e-6
+ * per output (the accumulation is fp32; the result is deterministic run to
+ * run).  One kernel.  Workspace: none (ws may be NULL). */
+int32_t tq2_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N,
+                 int64_t K, const uint16_t *x, float *y, void *ws,
+                 size_t ws_bytes, tq2_stream_t stream);
+
+/* tq2_gemv_gate_up -- two matrices of the same shape [N][K] sharing one x
+ * (page "gemma4 wNa8o8 requires int8 activations": gate and up share their
+ * input).  y is [2][N]: row 0 = gate, row 1 = up.  Same arithmetic and
+ * accuracy as tq2_gemv; one kernel reads x once for both. */
+int32_t tq2_gemv_gate_up(const uint8_t *codes_g, const uint16_t *scales_g,
+                         const uint8_t *codes_u, const uint16_t *scales_u,
+                         int64_t N, int64_t K, const uint16_t *x, float *y,
+                         void *ws, size_t ws_bytes, tq2_stream_t stream);
+
+/* tq2_quantize_i8 -- static int8 activation quantization (page "gemma4
+ * wNa8o8 requires int8 activations": clamp(round(x/s), -128, 127)).
+ * Precisely: v = x/s as one IEEE fp32 division, rint (ties to even),
+ * clamped to [-128,127] before conversion.  s must be finite and > 0;
+ * non-finite x gives an unspecified x_q.  x_q[K] is int8 in natural order. */
+int32_t tq2_quantize_i8(const uint16_t *x, int64_t K, float s, int8_t *x_q,
+                        tq2_stream_t stream);
+
+/* tq2_gemv_i8q -- int8 matvec on pre-quantized activations x_q[K]
+ * (same page: the input scale, then an int8 x integer-weight product).
+ * Block partials P[n][b] = sum_{k in b} x_q[k]*(q[n][k]-1) are exact
+ * integers; the output is defined order-free as
+ *   A_n = sum_b (d_nb * 2^24) * P[n][b]   (exact, int64)
+ *   y_n = fp32( fp64( fp64(A_n) * (double)s ) * 2^-24 ),
+ * which equals sum_b d_b*s*P[n][b] up to that final rounding and is
+ * bit-exact run to run.  K <= TQ2_I8_MAX_K.  partials (nullable): receives
+ * P as int32 [N][K/256].  Workspace: tq2_workspace_bytes(TQ2_OP_GEMV_I8Q).
+ * Two kernels (activation staging, matvec). */
+int32_t tq2_gemv_i8q(const uint8_t *codes, const uint16_t *scales,
+                     int64_t N, int64_t K, const int8_t *x_q, float s,
+                     float *y, int32_t *partials, void *ws, size_t ws_bytes,
+                     tq2_stream_t stream);
+
+/* tq2_gemv_i8 -- tq2_quantize_i8 then tq2_gemv_i8q, with the quantized
+ * activations kept in the workspace.  Workspace:
+ * tq2_workspace_bytes(TQ2_OP_GEMV_I8).  Two kernels. */
+int32_t tq2_gemv_i8(const uint8_t *codes, const uint16_t *scales, int64_t N,
+                    int64_t K, const uint16_t *x, float s, float *y, void *ws,
+                    size_t ws_bytes, tq2_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ2_H */

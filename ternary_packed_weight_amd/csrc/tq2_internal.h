@@ -1,0 +1,49 @@
+// Internal launch interface between the C ABI (tq2_api.cpp) and the gfx950
+// kernels (tq2_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tq2 {
+
+constexpr int64_t kBlock = 256;    // weights per block, one fp16 scale each
+constexpr int64_t kLaneK = 64;     // weights one lane decodes per 16-byte load
+constexpr int64_t kChunk = 4096;   // weights one wave64 covers per step
+
+__host__ __device__ inline int64_t chunks_of(int64_t K) { return (K + kChunk - 1) / kChunk; }
+
+// Up to three weight matrices that share K and the activation vector; their
+// outputs are concatenated in y (matrix m, row n -> y[row_begin[m] + n]).
+struct MatSet {
+  const uint8_t* codes[3];
+  const uint16_t* scales[3];
+  int64_t row_begin[3];
+  int32_t nmat;
+  int64_t rows;  // total rows over all matrices
+};
+
+// Workspace of the int8 path: permuted x_q (4 KiB per chunk) + per-lane
+// block-sum seeds (256 B per chunk).
+inline size_t i8_workspace_bytes(int64_t K) {
+  size_t b = (size_t)chunks_of(K) * (4096 + 256);
+  return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* codes,
+                       uint16_t* scales, int32_t* bad, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales,
+                          int64_t N, int64_t K, float* W, hipStream_t s);
+hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x,
+                           float* y, hipStream_t s);
+hipError_t launch_quantize_i8(const uint16_t* x, int64_t K, float scale,
+                              int8_t* xq, hipStream_t s);
+// Stage activations for the int8 matvec into `ws`: from fp16 x (quantizing
+// on the way) when x != nullptr, else from pre-quantized xq.
+hipError_t launch_i8_stage(const uint16_t* x, const int8_t* xq, int64_t K,
+                           float scale, void* ws, hipStream_t s);
+hipError_t launch_gemv_i8(const MatSet& m, int64_t K, const void* ws,
+                          float scale, float* y, int32_t* partials,
+                          hipStream_t s);
+
+}  // namespace tq2

@@ -1,0 +1,133 @@
+"""Host-side checks of libtq2: it loads, exports every function include/tq2.h
+declares, and rejects invalid arguments with the documented status before
+any launch.  Fake (never dereferenced) device addresses are used, so these
+tests only run where no GPU is visible."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq2.h")
+
+
+def _lib_path():
+    from ternary_packed_weight_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    return build.LIB
+
+
+@pytest.fixture(scope="module")
+def tq2():
+    _lib_path()
+    from ternary_packed_weight_amd import tq2 as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("tq2_pack", "tq2_gemv", "tq2_gemv_gate_up", "tq2_gemv_i8", "tq2_gemv_i8q",
+                     "tq2_quantize_i8", "tq2_dequant", "tq2_workspace_bytes"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(tq2):
+    lib = ctypes.CDLL(_lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in tq2.EXPORTED, name
+    assert tq2.tq2_abi_version() == 1
+
+
+def test_sizes(tq2):
+    assert tq2.tq2_codes_bytes(4096, 4096) == 4096 * 1024
+    assert tq2.tq2_scales_bytes(4096, 4096) == 4096 * 16 * 2
+    assert tq2.tq2_codes_bytes(1, 100) == 0
+    assert tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV, 4096, 4096) == 0
+    assert tq2.tq2_workspace_bytes(tq2.TQ2_OP_GATE_UP, 16384, 4096) == 0
+    ws = tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV_I8, 4096, 16384)
+    assert ws >= 16384 + 256 * 4 and ws % 256 == 0
+    assert tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV_I8, 4096, 65536) == 2 ** 64 - 1
+    assert tq2.tq2_workspace_bytes(99, 1, 256) == 2 ** 64 - 1
+    for s in range(7):
+        assert isinstance(tq2.tq2_status_string(s), str)
+
+
+no_gpu = pytest.mark.skipif(
+    __import__("torch").cuda.is_available(),
+    reason="fake device addresses are only safe to pass where no GPU exists")
+
+A = 1 << 30  # fake, 256-aligned, never dereferenced
+
+
+def P(addr):
+    return ctypes.c_void_p(addr)
+
+
+@no_gpu
+def test_error_paths_gemv(tq2):
+    lib = tq2.lib()
+    g = lambda c=A, s=A + 2 ** 24, N=16, K=256, x=A + 2 ** 25, y=A + 2 ** 26: lib.tq2_gemv(
+        P(c), P(s), N, K, P(x), P(y), None, 0, None)
+    assert g(N=0) == 1 and g(N=-3) == 1
+    assert g(K=0) == 2 and g(K=100) == 2 and g(K=384) == 2 and g(K=65536 + 256) == 2
+    assert g(N=2 ** 31, K=65536) == 2
+    assert g(c=0) == 1 and g(x=0) == 1 and g(y=0) == 1
+    assert g(c=A + 8) == 3 and g(s=A + 2 ** 24 + 1) == 3 and g(x=A + 2 ** 25 + 4) == 3
+    assert g(y=A + 2 ** 26 + 2) == 3
+    assert g(y=A + 8) == 1                     # y inside codes
+    assert g(y=A + 2 ** 25 - 16) == 1          # y overlapping x... codes plane is 1 KiB
+    gu = lib.tq2_gemv_gate_up(P(A), P(A + 4096), P(0), P(A + 8192), 16, 256, P(A + 2 ** 25),
+                              P(A + 2 ** 26), None, 0, None)
+    assert gu == 1
+
+
+@no_gpu
+def test_error_paths_int8(tq2):
+    lib = tq2.lib()
+    ws_need = tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV_I8, 16, 256)
+
+    def g(N=16, K=256, s=0.5, ws=A + 2 ** 27, wsb=ws_need, x=A + 2 ** 25, y=A + 2 ** 26):
+        return lib.tq2_gemv_i8(P(A), P(A + 2 ** 24), N, K, P(x), ctypes.c_float(s), P(y), P(ws), wsb, None)
+
+    assert g(K=65280 + 256) == 2
+    assert g(s=0.0) == 5 and g(s=-1.0) == 5 and g(s=float("inf")) == 5 and g(s=float("nan")) == 5
+    assert g(ws=0) == 4 and g(wsb=ws_need - 1) == 4
+    assert g(ws=A + 2 ** 27 + 128) == 3
+    assert g(ws=A) == 1                        # workspace overlaps codes
+    assert g(x=0) == 1
+    q = lib.tq2_gemv_i8q(P(A), P(A + 2 ** 24), 16, 256, P(0), ctypes.c_float(1.0), P(A + 2 ** 26),
+                         None, P(A + 2 ** 27), ws_need, None)
+    assert q == 1
+    q = lib.tq2_gemv_i8q(P(A), P(A + 2 ** 24), 16, 256, P(A + 2 ** 25), ctypes.c_float(1.0),
+                         P(A + 2 ** 26), P(A + 2 ** 26 + 2), P(A + 2 ** 27), ws_need, None)
+    assert q == 3                              # partials misaligned
+    q = lib.tq2_gemv_i8q(P(A), P(A + 2 ** 24), 16, 256, P(A + 2 ** 25), ctypes.c_float(1.0),
+                         P(A + 2 ** 26), P(A + 2 ** 26), P(A + 2 ** 27), ws_need, None)
+    assert q == 1                              # partials alias y
+    assert lib.tq2_quantize_i8(P(A), 256, ctypes.c_float(0.0), P(A + 4096), None) == 5
+    assert lib.tq2_quantize_i8(P(A), 255, ctypes.c_float(1.0), P(A + 4096), None) == 2
+    assert lib.tq2_quantize_i8(P(A), 256, ctypes.c_float(1.0), P(A + 96), None) == 1
+    assert lib.tq2_quantize_i8(P(A), 256, ctypes.c_float(1.0), P(A + 4097), None) == 3
+
+
+@no_gpu
+def test_error_paths_pack(tq2):
+    lib = tq2.lib()
+    W, C, S, B = A, A + 2 ** 28, A + 2 ** 29, A + 2 ** 29 + 2 ** 20
+    assert lib.tq2_pack(P(W), 0, 256, P(C), P(S), P(B), None) == 1
+    assert lib.tq2_pack(P(W), 4, 200, P(C), P(S), P(B), None) == 2
+    assert lib.tq2_pack(P(W + 4), 4, 256, P(C), P(S), P(B), None) == 3
+    assert lib.tq2_pack(P(W), 4, 256, P(C), P(S), P(B + 2), None) == 3
+    assert lib.tq2_pack(P(W), 4, 256, P(W + 64), P(S), P(B), None) == 1
+    assert lib.tq2_pack(P(0), 4, 256, P(C), P(S), P(B), None) == 1
+    assert lib.tq2_dequant(P(C), P(S), 4, 256, P(0), None) == 1
+    assert lib.tq2_dequant(P(C), P(S), 4, 256, P(C), None) == 1

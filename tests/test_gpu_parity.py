@@ -1,0 +1,311 @@
+"""GPU parity: every entry point of libtq2 against the CPU oracle on the
+same seeded inputs.  Bit-exact for pack, dequant, the quantizer and the int8
+path; per-output tolerance 2e-3 * sum_k |d_b(k) x_k| + 1e-6 for the fp16
+path.  Inputs of every matvec are packed by the oracle (never by the GPU).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from ternary_packed_weight_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def tq2():
+    assert torch.cuda.is_available(), "GPU parity tests need the MI355X"
+    from ternary_packed_weight_amd import tq2 as mod
+    return mod
+
+
+def _ternary_W(q, d):
+    dd = np.repeat(d.astype(np.float32), 256, axis=1)
+    return (dd * (q.astype(np.float32) - 1.0)).astype(np.float32)
+
+
+def _packed(seed, N, K, outliers=False):
+    q, d, x = synth.problem(seed, N, K, outliers=outliers)
+    codes, scales, bad = oracle.pack(_ternary_W(q, d))
+    assert bad == 0
+    return q, codes, scales, x
+
+
+def _to_dev(codes, scales, x=None):
+    c = torch.from_numpy(codes).to(DEV)
+    s = torch.from_numpy(scales.view(np.float16)).to(DEV)
+    if x is None:
+        return c, s
+    return c, s, torch.from_numpy(np.ascontiguousarray(x, np.float16)).to(DEV)
+
+
+def _tol(scales, x, N, K):
+    d = np.abs(scales.view(np.float16).astype(np.float64)).reshape(N, K // 256)
+    ax = np.abs(x.astype(np.float64)).reshape(K // 256, 256).sum(axis=1)
+    return 2e-3 * (d * ax[None, :]).sum(axis=1) + 1e-6
+
+
+def _check_f16(y_gpu, y_ref, tol):
+    err = np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64))
+    bad = np.nonzero(err > tol)[0]
+    assert bad.size == 0, f"{bad.size} rows out of tolerance, first {bad[:5]}, err {err[bad[:5]]}, tol {tol[bad[:5]]}"
+    return float((err / tol).max())
+
+
+# ------------------------------------------------------------------ pack
+
+PACK_SHAPES = [(1, 256), (3, 768), (33, 4096), (256, 4096), (5, 16384), (7, 4352)]
+
+
+@pytest.mark.parametrize("N,K", PACK_SHAPES)
+def test_pack_ternary_bit_exact(tq2, N, K):
+    q, d, _ = synth.problem(100 + N, N, K)
+    W = _ternary_W(q, d)
+    c_ref, s_ref, bad_ref = oracle.pack(W)
+    c, s, bad = tq2.tq2_pack(torch.from_numpy(W).to(DEV))
+    torch.cuda.synchronize()
+    assert int(bad.item()) == bad_ref == 0
+    assert np.array_equal(c.cpu().numpy(), c_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), s_ref)
+
+
+@pytest.mark.parametrize("N,K", [(9, 1024), (64, 4096)])
+def test_pack_generic_bit_exact(tq2, N, K):
+    g = synth.rng(200 + N)
+    W = synth.dense_weight(g, N, K)
+    # ties: an element at exactly half the block scale, and tiny blocks whose
+    # scale is a binary16 subnormal or rounds to zero
+    W[0, 1] = np.float32(np.float16(np.abs(W[0, :256]).max())) / 2
+    W[1, :256] *= np.float32(1e-6)
+    W[2, 256:512] *= np.float32(1e-9)
+    W[3, :256] = 0.0
+    c_ref, s_ref, bad_ref = oracle.pack(W)
+    c, s, bad = tq2.tq2_pack(torch.from_numpy(W).to(DEV))
+    torch.cuda.synchronize()
+    assert int(bad.item()) == bad_ref == 0
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), s_ref)
+    assert np.array_equal(c.cpu().numpy(), c_ref)
+
+
+def test_pack_bad_block_count(tq2):
+    W = synth.dense_weight(synth.rng(300), 4, 1024)
+    W[0, 5] = np.inf
+    W[1, 600] = np.nan
+    W[2, 300:310] = 1e6
+    _, _, bad_ref = oracle.pack(W)
+    _, _, bad = tq2.tq2_pack(torch.from_numpy(W).to(DEV))
+    torch.cuda.synchronize()
+    assert bad_ref == 3 and int(bad.item()) == 3
+
+
+def test_dequant_exact(tq2):
+    q, codes, scales, _ = _packed(310, 37, 768)
+    c, s = _to_dev(codes, scales)
+    W = tq2.tq2_dequant(c, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.cpu().numpy(), oracle.dequant(codes, scales, 37, 768))
+
+
+# ------------------------------------------------------------ fp16 matvec
+
+GEMV_SHAPES = [(1, 256), (3, 256), (33, 768), (257, 4096), (256, 4096), (4096, 4096),
+               (5, 16384), (130, 4352), (64, 8192), (1000, 16384), (17, 65536)]
+
+
+@pytest.mark.parametrize("N,K", GEMV_SHAPES)
+def test_gemv_f16_parity(tq2, N, K):
+    _, codes, scales, x = _packed(400 + N + K, N, K)
+    c, s, xd = _to_dev(codes, scales, x)
+    y = tq2.tq2_gemv(c, s, xd)
+    torch.cuda.synchronize()
+    y_ref = oracle.gemv(codes, scales, N, K, synth.bits(x))
+    _check_f16(y.cpu().numpy(), y_ref, _tol(scales, x, N, K))
+
+
+def test_gemv_f16_outliers(tq2):
+    N, K = 4096, 4096
+    _, codes, scales, x = _packed(1002, N, K, outliers=True)
+    assert np.abs(x.astype(np.float32)).max() > 20
+    c, s, xd = _to_dev(codes, scales, x)
+    y = tq2.tq2_gemv(c, s, xd)
+    torch.cuda.synchronize()
+    _check_f16(y.cpu().numpy(), oracle.gemv(codes, scales, N, K, synth.bits(x)), _tol(scales, x, N, K))
+
+
+def test_gemv_f16_one_hot_exact(tq2):
+    """x = e_k for every k of two blocks: y = d(q-1) exactly.  Pins the field
+    order of the decode, and that binary16 subnormal operands are honoured."""
+    N, K = 33, 512
+    q, codes, scales, _ = _packed(500, N, K)
+    c, s = _to_dev(codes, scales)
+    d = scales.view(np.float16).astype(np.float32)
+    X = torch.zeros((K, K), dtype=torch.float16, device=DEV)
+    X.fill_diagonal_(1.0)
+    ys = [tq2.tq2_gemv(c, s, X[k].contiguous()) for k in range(K)]
+    torch.cuda.synchronize()
+    for k in range(K):
+        expect = d[:, k // 256] * (q[:, k].astype(np.float32) - 1)
+        assert np.array_equal(ys[k].cpu().numpy(), expect), k
+
+
+def test_gemv_f16_special_values(tq2):
+    N, K = 8, 1024
+    q, codes, scales, x = _packed(510, N, K)
+    # subnormal and large activations, and a subnormal block scale
+    x = x.copy()
+    x[:8] = np.array([6e-8, -6e-8, 1e-5, -3e-5, 60000, -60000, 0.0, -0.0], np.float16)
+    scales = scales.copy()
+    scales[0, 0] = 0x0001
+    scales[1, 1] = 0x7BFF
+    c, s, xd = _to_dev(codes, scales, x)
+    y = tq2.tq2_gemv(c, s, xd)
+    torch.cuda.synchronize()
+    _check_f16(y.cpu().numpy(), oracle.gemv(codes, scales, N, K, synth.bits(x)), _tol(scales, x, N, K))
+    # all codes 1 -> zero up to rounding: the zero point is factored out as
+    # the block sum of x, so the fp16 path cancels two fp32 sums (the int8
+    # path is exact)
+    ones = np.full((N, K // 4), 0x55, np.uint8)
+    c1, s1 = _to_dev(ones, scales)
+    y = tq2.tq2_gemv(c1, s1, xd)
+    torch.cuda.synchronize()
+    l1 = (_tol(scales, x, N, K) - 1e-6) / 2e-3
+    assert np.all(np.abs(y.cpu().numpy()) <= 1e-5 * l1)
+
+
+def test_gemv_f16_negation_and_determinism(tq2):
+    N, K = 300, 4096
+    q, codes, scales, x = _packed(520, N, K)
+    neg, _, _ = oracle.pack(_ternary_W((2 - q).astype(np.uint8), scales.view(np.float16)))
+    c, s, xd = _to_dev(codes, scales, x)
+    cn = torch.from_numpy(neg).to(DEV)
+    y1 = tq2.tq2_gemv(c, s, xd)
+    y2 = tq2.tq2_gemv(c, s, xd)
+    yn = tq2.tq2_gemv(cn, s, xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    tol = _tol(scales, x, N, K)
+    _check_f16(yn.cpu().numpy(), -oracle.gemv(codes, scales, N, K, synth.bits(x)), tol)
+    assert np.all(np.abs((yn + y1).cpu().numpy()) <= 1e-5 * (tol - 1e-6) / 2e-3)
+
+
+@pytest.mark.parametrize("N,K", [(3, 256), (100, 768), (2048, 4096)])
+def test_gate_up_parity(tq2, N, K):
+    _, cg, sg, x = _packed(600 + N, N, K)
+    _, cu, su, _ = _packed(700 + N, N, K)
+    dcg, dsg, xd = _to_dev(cg, sg, x)
+    dcu, dsu = _to_dev(cu, su)
+    y = tq2.tq2_gemv_gate_up(dcg, dsg, dcu, dsu, xd)
+    yg = tq2.tq2_gemv(dcg, dsg, xd)
+    yu = tq2.tq2_gemv(dcu, dsu, xd)
+    torch.cuda.synchronize()
+    yc = y.cpu().numpy()
+    assert yc.shape == (2, N)
+    _check_f16(yc[0], oracle.gemv(cg, sg, N, K, synth.bits(x)), _tol(sg, x, N, K))
+    _check_f16(yc[1], oracle.gemv(cu, su, N, K, synth.bits(x)), _tol(su, x, N, K))
+    # same per-row arithmetic as the single matvec
+    assert torch.equal(y[0], yg) and torch.equal(y[1], yu)
+
+
+def test_gate_up_full_size_sampled(tq2):
+    """Fused gate+up at 2 x 16384 x 4096 in the launch configuration the
+    bench times; the oracle checks 96 sampled rows of each matrix."""
+    N, K = 16384, 4096
+    _, cg, sg, x = _packed(1003, N, K)
+    g2 = synth.rng(1103)
+    qu = synth.codes(g2, N, K)
+    du = synth.scales(g2, N, K)
+    cu, su, _ = oracle.pack(_ternary_W(qu, du))
+    dcg, dsg, xd = _to_dev(cg, sg, x)
+    dcu, dsu = _to_dev(cu, su)
+    y = tq2.tq2_gemv_gate_up(dcg, dsg, dcu, dsu, xd)
+    torch.cuda.synchronize()
+    yc = y.cpu().numpy()
+    rows = np.unique(np.concatenate([synth.rng(5).choice(N, 94, replace=False), [0, N - 1]]))
+    for m, (cc, ss) in enumerate([(cg, sg), (cu, su)]):
+        ref = oracle.gemv(cc[rows], ss[rows], rows.size, K, synth.bits(x))
+        _check_f16(yc[m, rows], ref, _tol(ss[rows], x, rows.size, K))
+
+
+# ------------------------------------------------------------ int8 path
+
+def test_quantize_bit_exact(tq2):
+    K = 16384
+    x = synth.activations(synth.rng(800), K)
+    x = synth.add_outliers(synth.rng(801), x)
+    for div in (100, 200, 7):
+        s = np.float32(np.float32(np.abs(x.astype(np.float32)).max()) / np.float32(div))
+        xq = tq2.tq2_quantize_i8(torch.from_numpy(x).to(DEV), s)
+        torch.cuda.synchronize()
+        assert np.array_equal(xq.cpu().numpy(), oracle.quantize_i8(synth.bits(x), s)), div
+
+
+def test_quantize_ties_and_clamps(tq2):
+    vals = np.array([1.25, 1.75, -1.25, -1.75, 0.25, 0.75, 63.5, 63.75, 64.0, -64.0, -64.5,
+                     -63.75, 0.0, -0.0] + [0.0] * 242, np.float16)
+    for s in (0.5, 3.0, 0.1, 1.0 / 3.0):
+        xq = tq2.tq2_quantize_i8(torch.from_numpy(vals).to(DEV), np.float32(s))
+        torch.cuda.synchronize()
+        assert np.array_equal(xq.cpu().numpy(), oracle.quantize_i8(synth.bits(vals), np.float32(s))), s
+    # every finite binary16 value against the oracle for one scale
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    allh = np.where(np.isfinite(allh), allh, np.float16(0)).astype(np.float16)
+    xq = tq2.tq2_quantize_i8(torch.from_numpy(allh).to(DEV), np.float32(0.0371))
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), oracle.quantize_i8(synth.bits(allh), np.float32(0.0371)))
+
+
+I8_SHAPES = [(1, 256, 100), (3, 768, 100), (33, 4096, 200), (257, 4352, 100), (4096, 16384, 100),
+             (4096, 16384, 200), (11, 65280, 100)]
+
+
+@pytest.mark.parametrize("N,K,div", I8_SHAPES)
+def test_gemv_i8_bit_exact(tq2, N, K, div):
+    q, codes, scales, x = _packed(900 + N + div, N, K, outliers=(div == 200))
+    s = np.float32(np.float32(np.abs(x.astype(np.float32)).max()) / np.float32(div))
+    c, sc, xd = _to_dev(codes, scales, x)
+    y = tq2.tq2_gemv_i8(c, sc, xd, s)
+    xq = tq2.tq2_quantize_i8(xd, s)
+    P = torch.empty((N, K // 256), dtype=torch.int32, device=DEV)
+    y2 = tq2.tq2_gemv_i8q(c, sc, xq, s, partials=P)
+    torch.cuda.synchronize()
+    xq_ref = oracle.quantize_i8(synth.bits(x), s)
+    y_ref, P_ref = oracle.gemv_i8q(codes, scales, N, K, xq_ref, s)
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+    assert np.array_equal(P.cpu().numpy(), P_ref)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+    assert np.array_equal(y2.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+def test_gemv_i8_extreme_scales_and_one_hot(tq2):
+    N, K = 5, 512
+    q, codes, scales, _ = _packed(950, N, K)
+    scales = scales.copy()
+    scales[0, 0], scales[1, 1], scales[2, 0], scales[3, 1] = 0x7BFF, 0x0001, 0x0400, 0x3C00
+    c, sc = _to_dev(codes, scales)
+    s = np.float32(0.01)
+    X = torch.zeros((K, K), dtype=torch.float16, device=DEV)
+    X.fill_diagonal_(1.0)
+    ys = [tq2.tq2_gemv_i8(c, sc, X[k].contiguous(), s) for k in range(K)]
+    torch.cuda.synchronize()
+    for k in range(K):
+        xq = np.zeros(K, np.int8)
+        xq[k] = 100
+        y_ref, _ = oracle.gemv_i8q(codes, scales, N, K, xq, s)
+        assert np.array_equal(ys[k].cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), k
+
+
+def test_gemv_i8_determinism_and_negation(tq2):
+    N, K = 512, 16384
+    q, codes, scales, x = _packed(960, N, K)
+    neg, _, _ = oracle.pack(_ternary_W((2 - q).astype(np.uint8), scales.view(np.float16)))
+    s = np.float32(np.float32(np.abs(x.astype(np.float32)).max()) / np.float32(100))
+    c, sc, xd = _to_dev(codes, scales, x)
+    y1 = tq2.tq2_gemv_i8(c, sc, xd, s)
+    y2 = tq2.tq2_gemv_i8(c, sc, xd, s)
+    yn = tq2.tq2_gemv_i8(torch.from_numpy(neg).to(DEV), sc, xd, s)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(yn, -y1)
