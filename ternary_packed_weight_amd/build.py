@@ -11,6 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq2.so")
+PROBE_LIB = os.path.join(HERE, "libtq2probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = [os.path.join(CSRC, "tq2_kernels.hip"), os.path.join(CSRC, "tq2_api.cpp")]
 FLAGS = [
@@ -22,9 +23,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
+def _hipcc(sources, out, verbose, extra=()):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -33,8 +34,14 @@ def build(verbose: bool = False, extra=()) -> str:
     errs = [l for l in res.stderr.splitlines() if "error" in l]
     if errs:
         raise RuntimeError("\n".join(errs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Build libtq2.so (the library) and libtq2probe.so (bench calibration)."""
+    _hipcc([os.path.join(CSRC, "tq2_probes.hip")], PROBE_LIB, verbose, extra)
+    return _hipcc(SOURCES, LIB, verbose, extra)
 
 
 if __name__ == "__main__":

@@ -59,13 +59,6 @@ __device__ __forceinline__ int64_t wave_sum64(int64_t v) {
   return v;
 }
 
-__device__ __forceinline__ int mat_of(const MatSet& m, int64_t row) {
-  int i = 0;
-  if (m.nmat > 1 && row >= m.row_begin[1]) i = 1;
-  if (m.nmat > 2 && row >= m.row_begin[2]) i = 2;
-  return i;
-}
-
 // ------------------------------------------------------------------ pack
 // Page "BitCPM ternary (1.58-bit)", recovery paragraph: d_block = max|W|,
 // code = round(W/d)+1.  One wave per 256-block: lane l owns elements
@@ -159,6 +152,14 @@ hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales,
 
 // ------------------------------------------------------------ fp16 matvec
 //
+// Work split: a wave owns one 4096-wide K-chunk c of R consecutive rows
+// (lane l covers k = 4096c + 64l .. +63, a quarter of one 256-block).  A
+// workgroup holds C chunk-waves for each of S row groups (C = ceil(K/4096),
+// S = max(1, 4/C)), so a row's C partial sums meet in LDS and are added in
+// chunk order: the result is deterministic.  Each wave first issues all its
+// weight loads (R x 16 B per lane), then loads and rearranges its x chunk
+// while they are in flight.
+//
 // Decode of one 32-bit code word v (16 weights; byte m holds local weights
 // 4m+j at bits 2j):
 //   v  & (0x00030003 << 2j) -> halves carry weight j (byte 0) and 8+j (byte 2)
@@ -166,56 +167,40 @@ hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales,
 // Each masked half is a binary16 subnormal equal to q * 4^j * 2^-24, exact.
 // v_dot2_f32_f16 against the matching x pair gives sum x q * 4^j * 2^-24;
 // four accumulators (one per j) are combined with the exact power-of-two
-// weights 4^-j.  Subtracting the lane's x sum (folded into the seed) turns q into
-// q-1.  The staged x pairs are, per lane and per 16-weight group g,
+// weights 4^-j.  Subtracting the lane's x sum (folded into the seed) turns q
+// into q-1.  The x pairs a lane needs are, per 16-weight group g,
 //   pair[8g+2j+0] = (x[16g+j],   x[16g+8+j])
 //   pair[8g+2j+1] = (x[16g+4+j], x[16g+12+j]).
-// LDS layout per chunk c: 8 uint4 slots per lane, slot-major so that a wave
-// reading slot i touches 1 KiB of consecutive LDS (no bank conflicts), then
-// one float seed per lane: -(sum of the lane's 64 x) * 2^-24.
 
-struct F16Lds {
-  uint4* pairs;  // [chunks][8][64]
-  float* seeds;  // [chunks][64]
-};
+constexpr uint32_t kOnesF16x2 = 0x3C003C00u;  // (1.0, 1.0)
 
-__device__ __forceinline__ F16Lds f16_lds(uint4* base, int64_t chunks) {
-  F16Lds l;
-  l.pairs = base;
-  l.seeds = reinterpret_cast<float*>(base + chunks * 8 * 64);
-  return l;
-}
-
-__device__ void stage_x_f16(const uint16_t* __restrict__ x, int64_t K, F16Lds l) {
-  const int64_t lanes_total = K / kLaneK;
-  for (int64_t idx = threadIdx.x; idx < lanes_total; idx += blockDim.x) {
-    const int64_t c = idx >> 6;
-    const int lane = (int)(idx & 63);
-    const uint4* src = reinterpret_cast<const uint4*>(x + idx * kLaneK);
-    uint32_t xw[32];
+// Rearrange a lane's 64 fp16 activations (natural order, 32 dwords) into the
+// decode's operand pairs, and return -(sum of the 64 values) * 2^-24.
+__device__ __forceinline__ float x_pairs_f16(const uint32_t (&xw)[32], uint32_t (&xp)[32]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 t = src[i];
-      xw[4 * i + 0] = t.x; xw[4 * i + 1] = t.y; xw[4 * i + 2] = t.z; xw[4 * i + 3] = t.w;
-    }
-    auto xh = [&](int t) -> uint32_t { return (xw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu; };
-    uint32_t pr[32];
-    float sum = 0.0f;
+  for (int g = 0; g < 4; ++g) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pr[8 * g + 2 * j + 0] = xh(16 * g + j) | (xh(16 * g + 8 + j) << 16);
-        pr[8 * g + 2 * j + 1] = xh(16 * g + 4 + j) | (xh(16 * g + 12 + j) << 16);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = xw[8 * g + (j >> 1)], b = xw[8 * g + 4 + (j >> 1)];
+      const uint32_t c = xw[8 * g + 2 + (j >> 1)], d = xw[8 * g + 6 + (j >> 1)];
+      if (j & 1) {
+        xp[8 * g + 2 * j + 0] = (a >> 16) | (b & 0xFFFF0000u);
+        xp[8 * g + 2 * j + 1] = (c >> 16) | (d & 0xFFFF0000u);
+      } else {
+        xp[8 * g + 2 * j + 0] = (a & 0xFFFFu) | (b << 16);
+        xp[8 * g + 2 * j + 1] = (c & 0xFFFFu) | (d << 16);
       }
     }
-#pragma unroll
-    for (int t = 0; t < 64; ++t) sum += half_to_float((uint16_t)xh(t));
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      l.pairs[(c * 8 + i) * 64 + lane] = make_uint4(pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]);
-    l.seeds[c * 64 + lane] = -ldexpf(sum, -24);
   }
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    s0 = dot2(xw[i + 0], kOnesF16x2, s0);
+    s1 = dot2(xw[i + 1], kOnesF16x2, s1);
+    s2 = dot2(xw[i + 2], kOnesF16x2, s2);
+    s3 = dot2(xw[i + 3], kOnesF16x2, s3);
+  }
+  return -ldexpf((s0 + s1) + (s2 + s3), -24);
 }
 
 // sum_{64 weights} x * q * 2^-24 + seed, i.e. (lane partial of x(q-1)) * 2^-24
@@ -239,63 +224,184 @@ __device__ __forceinline__ float lane_dot_f16(const uint4 w, const uint32_t (&xp
   return fmaf(a3, 0.015625f, fmaf(a2, 0.0625f, fmaf(a1, 0.25f, a0)));
 }
 
-template <int R, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void k_gemv_f16(MatSet ms, int64_t K,
-                                                         const uint16_t* __restrict__ x,
-                                                         float* __restrict__ y) {
-  extern __shared__ uint4 lds_raw[];
-  const int64_t chunks = chunks_of(K);
-  const F16Lds l = f16_lds(lds_raw, chunks);
-  stage_x_f16(x, K, l);
-  __syncthreads();
+// ---- wave64 reduction of R per-lane values (one per row) ----
+// Transposed butterfly: v_permlane32_swap folds lanes 32..63 onto 0..31 for
+// two rows at once, v_permlane16_swap folds 16-lane rows likewise, and four
+// DPP row rotations finish inside each 16-lane row.  On return, out[i] in
+// 16-lane row rho (lanes 16rho..16rho+15, all equal) is the full sum of row
+//   i + (rho & 1) * (R/4) + (rho >> 1) * (R/2)     for R >= 4,
+//   rho >> 1                                         for R == 2.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
 
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                  __builtin_bit_cast(unsigned, b), false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                  __builtin_bit_cast(unsigned, b), false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0x128>(v);  // row_ror:8
+  v += dpp_f32<0x124>(v);  // row_ror:4
+  v += dpp_f32<0x122>(v);  // row_ror:2
+  v += dpp_f32<0x121>(v);  // row_ror:1
+  return v;
+}
+
+template <int R>
+__device__ __forceinline__ void reduce_rows_f32(float (&v)[R], float (&out)[R >= 4 ? R / 4 : 1]) {
+  static_assert(R == 2 || R == 4 || R == 8, "R must be 2, 4 or 8");
+  constexpr int H = R / 2;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    float a = v[i], b = v[i + H];
+    swap32(a, b);
+    v[i] = a + b;  // lanes 0..31: row i, lanes 32..63: row i+H
+  }
+  if constexpr (R == 2) {
+    float a = v[0], b = v[0];
+    swap16(a, b);
+    out[0] = row16_sum(a + b);
+  } else {
+    constexpr int Q = R / 4;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      float a = v[i], b = v[i + Q];
+      swap16(a, b);
+      out[i] = row16_sum(a + b);
+    }
+  }
+}
+
+template <int R>
+__device__ __forceinline__ int reduced_row(int i, int rho) {
+  if constexpr (R == 2) return rho >> 1;
+  else return i + (rho & 1) * (R / 4) + (rho >> 1) * (R / 2);
+}
+
+// Row base pointers.  `row` is wave-uniform, and only constant indices into
+// the kernel-argument arrays are used, so all of this stays in scalar
+// registers: the weight loads do not wait on a pointer fetch.
+struct RowPtr {
+  const uint8_t* codes;
+  const uint16_t* scales;
+};
+
+__device__ __forceinline__ RowPtr row_ptr(const MatSet& ms, int64_t row, int64_t row_bytes,
+                                          int64_t BK) {
+  int64_t lr = row;
+  const uint8_t* c = ms.codes[0];
+  const uint16_t* s = ms.scales[0];
+  if (ms.nmat > 1 && row >= ms.row_begin[1]) {
+    lr = row - ms.row_begin[1];
+    c = ms.codes[1];
+    s = ms.scales[1];
+  }
+  if (ms.nmat > 2 && row >= ms.row_begin[2]) {
+    lr = row - ms.row_begin[2];
+    c = ms.codes[2];
+    s = ms.scales[2];
+  }
+  return RowPtr{c + lr * row_bytes, s + lr * BK};
+}
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Weights are read exactly once: stream them past the caches.
+__device__ __forceinline__ uint4 load_codes(const uint8_t* p) {
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+template <int R, int MAXT>
+__global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
+                                                   const uint16_t* __restrict__ x,
+                                                   float* __restrict__ y, int C, int S) {
+  __shared__ float red[16][R];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t groups = (ms.rows + R - 1) / R;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = wave % C;
+  const int slot = wave / C;
+  const int64_t row0 = ((int64_t)blockIdx.x * S + slot) * R;
+  const int64_t k0 = (int64_t)c * kChunk + (int64_t)lane * kLaneK;
+  const bool active = k0 < K;
   const int64_t row_bytes = K / 4;
   const int64_t BK = K / kBlock;
 
-  for (int64_t g = (int64_t)blockIdx.x * WAVES + wave; g < groups;
-       g += (int64_t)gridDim.x * WAVES) {
-    float acc[R];
+  // 1. every load is unconditional and in bounds (rows past the end read the
+  //    last row, lanes past K read k = 0) so that nothing waits on a branch;
+  //    those lanes and rows are zeroed afterwards through their scale.
+  //    The activations are requested first: memory counters retire in
+  //    order, so x can be rearranged while the weights are still in flight.
+  const int64_t kk = active ? k0 : 0;
+  uint32_t xw[32];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-
-    for (int64_t c = 0; c < chunks; ++c) {
-      const int64_t k0 = c * kChunk + (int64_t)lane * kLaneK;
-      if (k0 < K) {
-        uint4 w[R];
-        float d[R];
+  for (int i = 0; i < 8; ++i) {
+    const uint4 t = *reinterpret_cast<const uint4*>(x + kk + 8 * i);
+    xw[4 * i + 0] = t.x; xw[4 * i + 1] = t.y; xw[4 * i + 2] = t.z; xw[4 * i + 3] = t.w;
+  }
+  uint4 w[R];
+  uint16_t hs[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int64_t row = g * R + r;
-          if (row < ms.rows) {
-            const int m = mat_of(ms, row);
-            const int64_t lr = row - ms.row_begin[m];
-            w[r] = *reinterpret_cast<const uint4*>(ms.codes[m] + lr * row_bytes + k0 / 4);
-            d[r] = half_to_float(ms.scales[m][lr * BK + k0 / kBlock]);
-          } else {
-            w[r] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-            d[r] = 0.0f;
-          }
-        }
-        uint32_t xp[32];
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r < ms.rows ? row0 + r : ms.rows - 1;
+    const RowPtr rp = row_ptr(ms, row, row_bytes, BK);
+    w[r] = load_codes(rp.codes + kk / 4);
+    hs[r] = rp.scales[kk / kBlock];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the math
+  // 2. rearrange this lane's 64 activations into the decode's operand pairs
+  uint32_t xp[32];
+  const float seed = x_pairs_f16(xw, xp);
+  // 3. decode, block partial times its scale
+  float acc[R];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 t = l.pairs[(c * 8 + i) * 64 + lane];
-          xp[4 * i + 0] = t.x; xp[4 * i + 1] = t.y; xp[4 * i + 2] = t.z; xp[4 * i + 3] = t.w;
-        }
-        const float seed = l.seeds[c * 64 + lane];
+  for (int r = 0; r < R; ++r) {
+    // binary16 +0 for padding lanes and rows, by masking the bits (a select
+    // here would let the compiler sink the scale load into a branch)
+    const uint32_t keep = 0u - (uint32_t)(active && row0 + r < ms.rows);
+    const float d = half_to_float((uint16_t)(hs[r] & keep));
+    acc[r] = d * lane_dot_f16(w[r], xp, seed);
+  }
+  // 4. reduce over the wave
+  float out[R >= 4 ? R / 4 : 1];
+  reduce_rows_f32<R>(acc, out);
+  const int rho = lane >> 4;
+  constexpr int NOUT = R >= 4 ? R / 4 : 1;
+  if (C == 1) {
+    if ((lane & 15) == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = fmaf(d[r], lane_dot_f16(w[r], xp, seed), acc[r]);
+      for (int i = 0; i < NOUT; ++i) {
+        const int64_t row = row0 + reduced_row<R>(i, rho);
+        if (R != 2 || (rho & 1) == 0)
+          if (row < ms.rows) y[row] = ldexpf(out[i], 24);
       }
     }
+    return;
+  }
+  // 5. several chunk-waves per row: add their sums in chunk order
+  if ((lane & 15) == 0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float t = wave_sum(acc[r]);
-      const int64_t row = g * R + r;
-      if (lane == 0 && row < ms.rows) y[row] = ldexpf(t, 24);
-    }
+    for (int i = 0; i < NOUT; ++i)
+      if (R != 2 || (rho & 1) == 0) red[wave][reduced_row<R>(i, rho)] = out[i];
+  }
+  __syncthreads();
+  if (c == 0 && lane < R) {
+    float t = red[wave][lane];
+    for (int cc = 1; cc < C; ++cc) t += red[wave + cc][lane];
+    const int64_t row = row0 + lane;
+    if (row < ms.rows) y[row] = ldexpf(t, 24);
   }
 }
 
@@ -307,30 +413,37 @@ static int device_cus() {
   return cus;
 }
 
-template <int R, int WAVES>
-static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
-                               hipStream_t s, int wg_per_cu) {
-  const int64_t chunks = chunks_of(K);
-  const size_t lds = (size_t)chunks * (8 * 64 * 16 + 64 * 4);
-  static bool attr_set = false;  // raise the dynamic LDS cap once
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_f16<R, WAVES>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+// Rows per wave: as many as keep at least ~8 waves per CU busy (all weight
+// bytes are then in flight at once), at most 8.
+static int pick_rows_per_wave(int64_t rows, int C) {
+  const int64_t want_waves = (int64_t)device_cus() * 8;
+  for (int R : {8, 4}) {
+    if ((rows + R - 1) / R * C >= want_waves) return R;
   }
+  return 2;
+}
+
+template <int R>
+static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
+                               hipStream_t s) {
+  const int C = (int)chunks_of(K);
+  const int S = C >= 4 ? 1 : 4 / C;
   const int64_t groups = (m.rows + R - 1) / R;
-  int64_t grid = (groups + WAVES - 1) / WAVES;
-  const int64_t cap = (int64_t)device_cus() * wg_per_cu;
-  if (grid > cap) grid = cap;
-  hipLaunchKernelGGL((k_gemv_f16<R, WAVES>), dim3((unsigned)grid), dim3(64 * WAVES), lds, s,
-                     m, K, x, y);
+  const int64_t grid = (groups + S - 1) / S;
+  if (C * S <= 4)
+    hipLaunchKernelGGL((k_gemv_f16<R, 256>), dim3((unsigned)grid), dim3(64 * C * S), 0, s, m, K, x, y, C, S);
+  else
+    hipLaunchKernelGGL((k_gemv_f16<R, 1024>), dim3((unsigned)grid), dim3(64 * C * S), 0, s, m, K, x, y, C, S);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
                            hipStream_t s) {
-  return run_gemv_f16<8, 4>(m, K, x, y, s, 4);
+  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K))) {
+    case 8: return run_gemv_f16<8>(m, K, x, y, s);
+    case 4: return run_gemv_f16<4>(m, K, x, y, s);
+    default: return run_gemv_f16<2>(m, K, x, y, s);
+  }
 }
 
 // ------------------------------------------------------------ int8 path
@@ -450,97 +563,187 @@ __device__ __forceinline__ int64_t scaled_partial(uint16_t h, int P) {
   return (int64_t)t << sh;
 }
 
-template <int R, int WAVES, bool PARTIALS>
-__global__ __launch_bounds__(64 * WAVES) void k_gemv_i8(MatSet ms, int64_t K,
-                                                        const uint4* __restrict__ slots,
-                                                        const int32_t* __restrict__ seeds,
-                                                        float s, float* __restrict__ y,
-                                                        int32_t* __restrict__ partials) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t chunks = chunks_of(K);
-  const int64_t groups = (ms.rows + R - 1) / R;
-  const int64_t row_bytes = K / 4;
-  const int64_t BK = K / kBlock;
+// ---- the same transposed reduction for exact int64 sums ----
+__device__ __forceinline__ void swap32_i64(int64_t& a, int64_t& b) {
+  const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)a, (unsigned)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)((uint64_t)a >> 32),
+                                                   (unsigned)((uint64_t)b >> 32), false, false);
+  a = (int64_t)(((uint64_t)(unsigned)hi[0] << 32) | (unsigned)lo[0]);
+  b = (int64_t)(((uint64_t)(unsigned)hi[1] << 32) | (unsigned)lo[1]);
+}
 
-  for (int64_t g = (int64_t)blockIdx.x * WAVES + wave; g < groups;
-       g += (int64_t)gridDim.x * WAVES) {
-    int64_t acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0;
+__device__ __forceinline__ void swap16_i64(int64_t& a, int64_t& b) {
+  const auto lo = __builtin_amdgcn_permlane16_swap((unsigned)a, (unsigned)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((unsigned)((uint64_t)a >> 32),
+                                                   (unsigned)((uint64_t)b >> 32), false, false);
+  a = (int64_t)(((uint64_t)(unsigned)hi[0] << 32) | (unsigned)lo[0]);
+  b = (int64_t)(((uint64_t)(unsigned)hi[1] << 32) | (unsigned)lo[1]);
+}
 
-    for (int64_t c = 0; c < chunks; ++c) {
-      const int64_t k0 = c * kChunk + (int64_t)lane * kLaneK;
-      if (k0 < K) {
-        uint4 w[R];
-        uint16_t h[R];
+template <int CTRL>
+__device__ __forceinline__ int64_t dpp_i64(int64_t v) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)v, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)((uint64_t)v >> 32), CTRL,
+                                                            0xF, 0xF, false);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t row16_sum_i64(int64_t v) {
+  v += dpp_i64<0x128>(v);
+  v += dpp_i64<0x124>(v);
+  v += dpp_i64<0x122>(v);
+  v += dpp_i64<0x121>(v);
+  return v;
+}
+
+template <int R>
+__device__ __forceinline__ void reduce_rows_i64(int64_t (&v)[R], int64_t (&out)[R >= 4 ? R / 4 : 1]) {
+  static_assert(R == 2 || R == 4 || R == 8, "R must be 2, 4 or 8");
+  constexpr int H = R / 2;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int64_t row = g * R + r;
-          if (row < ms.rows) {
-            const int m = mat_of(ms, row);
-            const int64_t lr = row - ms.row_begin[m];
-            w[r] = *reinterpret_cast<const uint4*>(ms.codes[m] + lr * row_bytes + k0 / 4);
-            h[r] = ms.scales[m][lr * BK + k0 / kBlock];
-          } else {
-            w[r] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-            h[r] = 0;
-          }
-        }
-        uint32_t xq[16];
+  for (int i = 0; i < H; ++i) {
+    int64_t a = v[i], b = v[i + H];
+    swap32_i64(a, b);
+    v[i] = a + b;
+  }
+  if constexpr (R == 2) {
+    int64_t a = v[0], b = v[0];
+    swap16_i64(a, b);
+    out[0] = row16_sum_i64(a + b);
+  } else {
+    constexpr int Q = R / 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 t = slots[(c * 4 + i) * 64 + lane];
-          xq[4 * i + 0] = t.x; xq[4 * i + 1] = t.y; xq[4 * i + 2] = t.z; xq[4 * i + 3] = t.w;
-        }
-        const int seed = seeds[c * 64 + lane];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int P = lane_dot_i8(w[r], xq, seed);
-          acc[r] += scaled_partial(h[r], P);
-          if (PARTIALS) {
-            // a 256-block spans lanes 4i..4i+3 of this chunk
-            int bp = P + __shfl_xor(P, 1, 64);
-            bp += __shfl_xor(bp, 2, 64);
-            const int64_t row = g * R + r;
-            if ((lane & 3) == 0 && row < ms.rows) partials[row * BK + k0 / kBlock] = bp;
-          }
-        }
-      }  // K % 256 == 0, so a quad of lanes is all inside or all outside K
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t A = wave_sum64(acc[r]);
-      const int64_t row = g * R + r;
-      if (lane == 0 && row < ms.rows) {
-        const double hi = (double)(int32_t)((uint64_t)A >> 32);
-        const double lo = (double)(uint32_t)((uint64_t)A & 0xFFFFFFFFu);
-        const double a = hi * 4294967296.0 + lo;  // one rounding: fp64(A)
-        y[row] = (float)((a * (double)s) * 0x1p-24);
-      }
+    for (int i = 0; i < Q; ++i) {
+      int64_t a = v[i], b = v[i + Q];
+      swap16_i64(a, b);
+      out[i] = row16_sum_i64(a + b);
     }
   }
 }
 
-template <int R, int WAVES, bool PARTIALS>
+// y = fl32(fl64(fl64(A) * s) * 2^-24); fl64(A) is formed as hi*2^32 + lo in
+// one rounding.
+__device__ __forceinline__ float i8_epilogue(int64_t A, float s) {
+  const double hi = (double)(int32_t)((uint64_t)A >> 32);
+  const double lo = (double)(uint32_t)((uint64_t)A & 0xFFFFFFFFu);
+  const double a = hi * 4294967296.0 + lo;
+  return (float)((a * (double)s) * 0x1p-24);
+}
+
+// Same work split as the fp16 matvec.  Activations come pre-arranged from the
+// staging kernel (4 x 16 B + one seed per lane and chunk), so a wave needs no
+// permutation.  Partials are exact, the cross-wave sum is exact, hence the
+// output does not depend on the reduction order at all.
+template <int R, bool PARTIALS, int MAXT>
+__global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
+                                                  const uint4* __restrict__ slots,
+                                                  const int32_t* __restrict__ seeds, float s,
+                                                  float* __restrict__ y,
+                                                  int32_t* __restrict__ partials, int C, int S) {
+  __shared__ int64_t red[16][R];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = wave % C;
+  const int slot = wave / C;
+  const int64_t row0 = ((int64_t)blockIdx.x * S + slot) * R;
+  const int64_t k0 = (int64_t)c * kChunk + (int64_t)lane * kLaneK;
+  const bool active = k0 < K;
+  const int64_t row_bytes = K / 4;
+  const int64_t BK = K / kBlock;
+
+  // unconditional in-bounds loads, masked afterwards (see the fp16 matvec)
+  const int64_t kk = active ? k0 : 0;
+  uint32_t xq[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 t = slots[((int64_t)c * 4 + i) * 64 + lane];
+    xq[4 * i + 0] = t.x; xq[4 * i + 1] = t.y; xq[4 * i + 2] = t.z; xq[4 * i + 3] = t.w;
+  }
+  const int seed = seeds[(int64_t)c * 64 + lane];
+  uint4 w[R];
+  uint16_t hs[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r < ms.rows ? row0 + r : ms.rows - 1;
+    const RowPtr rp = row_ptr(ms, row, row_bytes, BK);
+    w[r] = load_codes(rp.codes + kk / 4);
+    hs[r] = rp.scales[kk / kBlock];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the math
+
+  int64_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int P = lane_dot_i8(w[r], xq, seed);
+    const uint32_t keep = 0u - (uint32_t)(active && row0 + r < ms.rows);
+    const uint16_t h = (uint16_t)(hs[r] & keep);
+    acc[r] = scaled_partial(h, P);
+    if (PARTIALS) {
+      // a 256-block spans lanes 4i..4i+3 of this chunk
+      int bp = P + __shfl_xor(P, 1, 64);
+      bp += __shfl_xor(bp, 2, 64);
+      const int64_t row = row0 + r;
+      if (active && (lane & 3) == 0 && row < ms.rows) partials[row * BK + k0 / kBlock] = bp;
+    }
+  }
+  int64_t out[R >= 4 ? R / 4 : 1];
+  reduce_rows_i64<R>(acc, out);
+  const int rho = lane >> 4;
+  constexpr int NOUT = R >= 4 ? R / 4 : 1;
+  if (C == 1) {
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int i = 0; i < NOUT; ++i) {
+        const int64_t row = row0 + reduced_row<R>(i, rho);
+        if (R != 2 || (rho & 1) == 0)
+          if (row < ms.rows) y[row] = i8_epilogue(out[i], s);
+      }
+    }
+    return;
+  }
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < NOUT; ++i)
+      if (R != 2 || (rho & 1) == 0) red[wave][reduced_row<R>(i, rho)] = out[i];
+  }
+  __syncthreads();
+  if (c == 0 && lane < R) {
+    int64_t t = red[wave][lane];
+    for (int cc = 1; cc < C; ++cc) t += red[wave + cc][lane];
+    const int64_t row = row0 + lane;
+    if (row < ms.rows) y[row] = i8_epilogue(t, s);
+  }
+}
+
+template <int R, bool PARTIALS>
 static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const void* ws, float s, float* y,
-                              int32_t* partials, hipStream_t st, int wg_per_cu) {
-  const int64_t chunks = chunks_of(K);
+                              int32_t* partials, hipStream_t st) {
+  const int C = (int)chunks_of(K);
+  const int S = C >= 4 ? 1 : 4 / C;
   const uint4* slots = reinterpret_cast<const uint4*>(ws);
-  const int32_t* seeds = reinterpret_cast<const int32_t*>(slots + chunks * 4 * 64);
+  const int32_t* seeds = reinterpret_cast<const int32_t*>(slots + (int64_t)C * 4 * 64);
   const int64_t groups = (m.rows + R - 1) / R;
-  int64_t grid = (groups + WAVES - 1) / WAVES;
-  const int64_t cap = (int64_t)device_cus() * wg_per_cu;
-  if (grid > cap) grid = cap;
-  hipLaunchKernelGGL((k_gemv_i8<R, WAVES, PARTIALS>), dim3((unsigned)grid), dim3(64 * WAVES), 0,
-                     st, m, K, slots, seeds, s, y, partials);
+  const int64_t grid = (groups + S - 1) / S;
+  if (C * S <= 4)
+    hipLaunchKernelGGL((k_gemv_i8<R, PARTIALS, 256>), dim3((unsigned)grid), dim3(64 * C * S), 0, st,
+                       m, K, slots, seeds, s, y, partials, C, S);
+  else
+    hipLaunchKernelGGL((k_gemv_i8<R, PARTIALS, 1024>), dim3((unsigned)grid), dim3(64 * C * S), 0, st,
+                       m, K, slots, seeds, s, y, partials, C, S);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_i8(const MatSet& m, int64_t K, const void* ws, float scale, float* y,
                           int32_t* partials, hipStream_t s) {
-  if (partials) return run_gemv_i8<4, 4, true>(m, K, ws, scale, y, partials, s, 4);
-  return run_gemv_i8<8, 4, false>(m, K, ws, scale, y, partials, s, 4);
+  const int R = pick_rows_per_wave(m.rows, (int)chunks_of(K));
+  if (partials) {
+    if (R == 8) return run_gemv_i8<8, true>(m, K, ws, scale, y, partials, s);
+    if (R == 4) return run_gemv_i8<4, true>(m, K, ws, scale, y, partials, s);
+    return run_gemv_i8<2, true>(m, K, ws, scale, y, partials, s);
+  }
+  if (R == 8) return run_gemv_i8<8, false>(m, K, ws, scale, y, partials, s);
+  if (R == 4) return run_gemv_i8<4, false>(m, K, ws, scale, y, partials, s);
+  return run_gemv_i8<2, false>(m, K, ws, scale, y, partials, s);
 }
 
 }  // namespace tq2
