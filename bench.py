@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the TQ2_0 ternary decode matvec on one MI355X.
+
+Step = one decode step of the MiniCPM4-8B-shaped linear stack: 32 layers x
+(q 4096x4096, k 256x4096, v 256x4096, o 4096x4096, gate 16384x4096,
+up 16384x4096, down 4096x16384), i.e. 224 `tq2_gemv` dispatches back to back
+on one stream, each with its own fresh fp16 x.  The 224 dispatches are
+captured once as a HIP graph and the graph is replayed once per step.  Inputs
+(1.955 GB of packed weights, the activations and outputs) are resident in
+HBM before the timed region.  Weights are drawn on the GPU from seeded
+generators (codes P = 0.3/0.4/0.3, fp16 scales U[0.005, 0.05], x ~ N(0,1))
+and packed by `tq2_pack`.
+
+Printed: one JSON line with the whole-step HBM throughput (algorithmic
+bytes: 66/256 B per weight + 2 B per x element + 4 B per output), the
+roofline of the dominant kernel (the gate/up/down matvec instantiation,
+timed live with HIP events over back-to-back launches) and the CPU oracle
+timed on the host on a bounded sample (decode layer 0), which also serves as
+the parity gate: a mismatch prints passed=false and exits non-zero.
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--probes]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8.0 TB/s
+LAYERS = 32
+PROJ = [("q", 4096, 4096), ("k", 256, 4096), ("v", 256, 4096), ("o", 4096, 4096),
+        ("gate", 16384, 4096), ("up", 16384, 4096), ("down", 4096, 16384)]
+DOMINANT = ("gate", "up", "down")   # launches of the dominant kernel instantiation
+METRIC = "tq2_gemv achieved HBM GB/s and % of MI355X peak; 224-linear decode steps/sec"
+
+
+def algo_bytes(N, K):
+    """Algorithmic bytes of one matvec: 2-bit codes + one fp16 scale per 256
+    weights, the fp16 x read once, the fp32 y written once."""
+    return N * K * 66 // 256 + 2 * K + 4 * N
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_stack(tq2, synth, torch):
+    """Seeded weights of all 224 linears, packed on the GPU by tq2_pack."""
+    stack = []
+    host_layer0 = []
+    for l in range(LAYERS):
+        for p, (name, N, K) in enumerate(PROJ):
+            q, d, _ = synth.torch_problem(10000 + 7 * l + p, N, K)
+            W = d.float().repeat_interleave(256, dim=1) * (q.float() - 1.0)
+            codes, scales, bad = tq2.tq2_pack(W)
+            del W
+            x = synth.torch_activations(20000 + 7 * l + p, K)
+            y = torch.empty(N, dtype=torch.float32, device="cuda")
+            stack.append(dict(name=name, N=N, K=K, codes=codes, scales=scales, x=x, y=y, bad=bad))
+            if l == 0:
+                host_layer0.append(dict(name=name, N=N, K=K, q=q.cpu().numpy(),
+                                        d=d.cpu().numpy(), x=x.cpu().numpy()))
+            del q, d
+    torch.cuda.synchronize()
+    bad = sum(int(e["bad"].item()) for e in stack)
+    if bad:
+        raise RuntimeError(f"tq2_pack reported {bad} bad blocks on synthetic weights")
+    return stack, host_layer0
+
+
+def capture(torch, launches):
+    """Capture a list of launches into one HIP graph (after an eager warm-up)."""
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        for f in launches:
+            f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for f in launches:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps):
+    """Per-replay time in microseconds, HIP events around `reps` replays."""
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("tq2_kernels.hip", "tq2_internal.h"):
+        with open(os.path.join(ROOT, "ternary_packed_weight_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(sha):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "gemv_f16_gate_up_down_decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_leg(host_layer0, ys_layer0, min_seconds):
+    """Time the CPU oracle on decode layer 0 (7 linears) and check the GPU's
+    outputs of that layer against it (per-row tolerance
+    2e-3 * sum_k |d_b(k) x_k| + 1e-6)."""
+    import numpy as np
+
+    import oracle
+    from ternary_packed_weight_amd import synth
+
+    packed = []
+    for e in host_layer0:
+        dd = np.repeat(e["d"].astype(np.float32), 256, axis=1)
+        W = (dd * (e["q"].astype(np.float32) - 1.0)).astype(np.float32)
+        codes, scales, bad = oracle.pack(W)
+        del W, dd
+        packed.append((e, codes, scales))
+    layer_bytes = sum(algo_bytes(e["N"], e["K"]) for e in host_layer0)
+    reps, t0 = 0, time.perf_counter()
+    refs = None
+    while True:
+        out = [oracle.gemv(c, s, e["N"], e["K"], synth.bits(e["x"])) for (e, c, s) in packed]
+        refs = refs or out
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    worst = 0.0
+    ok = True
+    for (e, c, s), yr, yg in zip(packed, refs, ys_layer0):
+        d = np.abs(s.view(np.float16).astype(np.float64))
+        ax = np.abs(e["x"].astype(np.float64)).reshape(-1, 256).sum(axis=1)
+        tol = 2e-3 * (d * ax[None, :]).sum(axis=1) + 1e-6
+        err = np.abs(yg.astype(np.float64) - yr.astype(np.float64))
+        worst = max(worst, float((err / tol).max()))
+        ok = ok and bool(np.all(err <= tol))
+    cpu = {"value": round(layer_bytes * reps / dt / 1e9, 4), "unit": "GB/s",
+           "cores": oracle.threads(), "kind": "oracle",
+           "sample": f"decode layer 0 (7 linears, {sum(e['N'] * e['K'] for e in host_layer0)} weights) "
+                     f"x {reps} passes in {dt:.1f} s; plain C oracle, fp64 accumulation, OpenMP over rows"}
+    nout = sum(e["N"] for e in host_layer0)
+    parity = {"passed": ok, "checked": f"all {nout} outputs of decode layer 0 vs the CPU oracle",
+              "max_err_over_tol": round(worst, 6)}
+    return cpu, parity
+
+
+def run_probes(torch, nbytes=1 << 30):
+    """Calibration kernels of known size for hardware byte counters: a
+    read-only 16-byte stream over `nbytes` and a fill of nbytes/4."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "ternary_packed_weight_amd", "libtq2probe.so"))
+    lib.tq2probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                  ctypes.c_void_p]
+    lib.tq2probe_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32,
+                                  ctypes.c_void_p]
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        lib.tq2probe_fill(ctypes.c_void_p(buf.data_ptr()), nbytes // 4, 7, 2048, s)
+        lib.tq2probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), 2048, s)
+    torch.cuda.synchronize()
+    return {"read_bytes": nbytes, "fill_bytes": nbytes // 4}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg (and its parity gate)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--probes", action="store_true", help="also run the byte-counter calibration kernels")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from ternary_packed_weight_amd import synth
+    from ternary_packed_weight_amd import tq2
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    log(f"device: {torch.cuda.get_device_name(0)}; building the 224-linear stack")
+    t0 = time.time()
+    stack, host_layer0 = build_stack(tq2, synth, torch)
+    log(f"stack built and packed on the GPU in {time.time() - t0:.1f} s")
+
+    # ---- the step: 224 dispatches on one stream, as one graph
+    def launch(e):
+        return lambda: tq2.tq2_gemv(e["codes"], e["scales"], e["x"], y=e["y"])
+
+    step_graph = capture(torch, [launch(e) for e in stack])
+    for _ in range(args.warmup):
+        step_graph.replay()
+    torch.cuda.synchronize()                       # barrier (one rank) + sync
+    t_start = time.perf_counter()
+    us_step = time_graph(torch, step_graph, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_bytes = sum(algo_bytes(e["N"], e["K"]) for e in stack)
+    gbs = step_bytes / us_step / 1e3
+    log(f"step: {us_step:.1f} us ({1e6 / us_step:.0f} steps/s), {gbs:.1f} GB/s; wall {wall:.3f} s")
+
+    # ---- dominant kernel: the gate/up/down launches back to back
+    dom = [e for e in stack if e["name"] in DOMINANT]
+    dom_graph = capture(torch, [launch(e) for e in dom])
+    dom_graph.replay()
+    us_dom = time_graph(torch, dom_graph, max(3, args.steps // 2)) / len(dom)
+    dom_bytes = sum(algo_bytes(e["N"], e["K"]) for e in dom) / len(dom)
+    achieved = dom_bytes / us_dom / 1e3
+    sha = kernel_source_sha()
+    traffic = traffic_from_profiles(sha)
+    roofline = {"bound": "hbm", "kernel": "tq2::k_gemv_f16<4,512> (gate, up, down)",
+                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "bytes_per_launch": int(dom_bytes), "us_per_launch": round(us_dom, 3),
+                "launches_timed": len(dom), "kernel_source_sha": sha}
+    log(f"dominant kernel: {us_dom:.2f} us/launch, {achieved:.1f} GB/s ({achieved / PEAK_HBM_GBS:.1%})")
+
+    if args.probes:
+        # eager launches too, so per-dispatch counters see the dominant kernel
+        for e in dom:
+            launch(e)()
+        torch.cuda.synchronize()
+        run_probes(torch)
+
+    cpu, parity = None, None
+    if not args.no_cpu:
+        ys0 = [stack[i]["y"].cpu().numpy() for i in range(len(PROJ))]
+        cpu, parity = cpu_leg(host_layer0, ys0, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads; parity {parity}")
+
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "accumulate": "f32", "data": "synthetic",
+        "config": {"workload": "MiniCPM4-8B decode step: 224 TQ2_0 linears (32 layers x q,k,v,o "
+                               "4096/256/256/4096x4096, gate,up 16384x4096, down 4096x16384), fresh "
+                               "fp16 x per linear, one stream, one HIP graph per step",
+                   "bytes_per_step": step_bytes, "launches_per_step": len(stack),
+                   "parallelism": "single GPU"},
+        "steps_per_s": round(1e6 / us_step, 1),
+        "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+    if parity is not None and not parity["passed"]:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,8 +30,7 @@
  *   - Outputs must not alias inputs.
  *   - K must be a positive multiple of 256 and at most TQ2_MAX_K
  *     (TQ2_I8_MAX_K on the int8 path).  N is any value >= 1, N*K < 2^40.
- *   - Alignment: codes, x, x_q and W 16 bytes; scales 2; y, partials 4;
- *     workspace 256.
+ *   - Alignment: codes, x, x_q and W 16 bytes; scales 2; y, partials 4.
  */
 #ifndef TQ2_H
 #define TQ2_H
@@ -78,8 +77,11 @@ const char *tq2_status_string(int32_t status);
 size_t tq2_codes_bytes(int64_t N, int64_t K);
 size_t tq2_scales_bytes(int64_t N, int64_t K);
 
-/* Device workspace an operation needs, in bytes (0 = none; pass NULL).
- * `op` is a tq2_op; for TQ2_OP_GATE_UP, N is the row count of one matrix.  Returns (size_t)-1 for an invalid op or shape. */
+/* Device workspace an operation needs, in bytes.  Every operation of this
+ * version needs none (0: pass ws = NULL, ws_bytes = 0); the arguments are
+ * kept so that a split-K variant can take scratch without an ABI change.
+ * `op` is a tq2_op; for TQ2_OP_GATE_UP, N is the row count of one matrix.
+ * Returns (size_t)-1 for an invalid op or shape. */
 size_t tq2_workspace_bytes(int32_t op, int64_t N, int64_t K);
 
 /* tq2_pack -- fp32 W[N][K] (row-major) -> codes + scales.
@@ -138,16 +140,15 @@ int32_t tq2_quantize_i8(const uint16_t *x, int64_t K, float s, int8_t *x_q,
  *   y_n = fp32( fp64( fp64(A_n) * (double)s ) * 2^-24 ),
  * which equals sum_b d_b*s*P[n][b] up to that final rounding and is
  * bit-exact run to run.  K <= TQ2_I8_MAX_K.  partials (nullable): receives
- * P as int32 [N][K/256].  Workspace: tq2_workspace_bytes(TQ2_OP_GEMV_I8Q).
- * Two kernels (activation staging, matvec). */
+ * P as int32 [N][K/256].  One kernel; no workspace. */
 int32_t tq2_gemv_i8q(const uint8_t *codes, const uint16_t *scales,
                      int64_t N, int64_t K, const int8_t *x_q, float s,
                      float *y, int32_t *partials, void *ws, size_t ws_bytes,
                      tq2_stream_t stream);
 
-/* tq2_gemv_i8 -- tq2_quantize_i8 then tq2_gemv_i8q, with the quantized
- * activations kept in the workspace.  Workspace:
- * tq2_workspace_bytes(TQ2_OP_GEMV_I8).  Two kernels. */
+/* tq2_gemv_i8 -- tq2_quantize_i8 then tq2_gemv_i8q, fused: the matvec
+ * kernel quantizes x itself (same definition, bit for bit) and keeps x_q on
+ * chip.  One kernel; no workspace. */
 int32_t tq2_gemv_i8(const uint8_t *codes, const uint16_t *scales, int64_t N,
                     int64_t K, const uint16_t *x, float s, float *y, void *ws,
                     size_t ws_bytes, tq2_stream_t stream);

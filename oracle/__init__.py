@@ -50,6 +50,8 @@ def _lib():
         lib.oracle_gemv_i8q.restype = None
         lib.oracle_gemv_i8.argtypes = [P, P, I64, I64, P, ctypes.c_float, P]
         lib.oracle_gemv_i8.restype = None
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -62,6 +64,11 @@ def _c(a, dtype):
 def _shape_check(N, K):
     if N < 1 or K < 256 or K % 256:
         raise ValueError(f"bad shape N={N} K={K}")
+
+
+def threads() -> int:
+    """Threads the oracle's row loops use (OpenMP)."""
+    return int(_lib().oracle_threads())
 
 
 def half_to_float(bits: int) -> float:

@@ -232,3 +232,11 @@ void oracle_gemv_i8(const uint8_t *codes, const uint16_t *scales, int64_t N,
     oracle_gemv_i8q(codes, scales, N, K, xq, s, y, NULL);
     free(xq);
 }
+
+/* Number of threads the OpenMP loops above run with. */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_threads(void) { return 1; }
+#endif

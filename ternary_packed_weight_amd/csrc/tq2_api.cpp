@@ -78,7 +78,7 @@ size_t tq2_workspace_bytes(int32_t op, int64_t N, int64_t K) {
       return check_shape(N, K, TQ2_MAX_K) == TQ2_OK ? 0 : (size_t)-1;
     case TQ2_OP_GEMV_I8:
     case TQ2_OP_GEMV_I8Q:
-      return check_shape(N, K, TQ2_I8_MAX_K) == TQ2_OK ? tq2::i8_workspace_bytes(K) : (size_t)-1;
+      return check_shape(N, K, TQ2_I8_MAX_K) == TQ2_OK ? 0 : (size_t)-1;
     default:
       return (size_t)-1;
   }
@@ -165,7 +165,7 @@ int32_t tq2_quantize_i8(const uint16_t* x, int64_t K, float s, int8_t* x_q, tq2_
 
 static int32_t i8_common(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                          const uint16_t* x, const int8_t* x_q, float s, float* y,
-                         int32_t* partials, void* ws, size_t ws_bytes, tq2_stream_t stream) {
+                         int32_t* partials, tq2_stream_t stream) {
   TQ2_TRY(check_shape(N, K, TQ2_I8_MAX_K));
   if ((!x && !x_q) || !y) return TQ2_ERR_ARG;
   TQ2_TRY(check_weights(codes, scales));
@@ -173,45 +173,42 @@ static int32_t i8_common(const uint8_t* codes, const uint16_t* scales, int64_t N
       (partials && !aligned(partials, 4)))
     return TQ2_ERR_ALIGN;
   TQ2_TRY(check_scale(s));
-  const size_t need = tq2::i8_workspace_bytes(K);
-  if (!ws || ws_bytes < need) return TQ2_ERR_WORKSPACE;
-  if (!aligned(ws, 256)) return TQ2_ERR_ALIGN;
   const size_t yb = (size_t)N * 4, pb = partials ? (size_t)(N * (K / 256)) * 4 : 0;
   const size_t cb = (size_t)(N * K / 4), sb = (size_t)(N * K / 128);
   const void* in_ptr = x ? (const void*)x : (const void*)x_q;
   const size_t in_b = x ? (size_t)K * 2 : (size_t)K;
-  const void* outs[3] = {y, partials, ws};
-  const size_t outb[3] = {yb, pb, need};
-  for (int i = 0; i < 3; ++i) {
+  const void* outs[2] = {y, partials};
+  const size_t outb[2] = {yb, pb};
+  for (int i = 0; i < 2; ++i)
     if (overlaps(outs[i], outb[i], codes, cb) || overlaps(outs[i], outb[i], scales, sb) ||
         overlaps(outs[i], outb[i], in_ptr, in_b))
       return TQ2_ERR_ARG;
-    for (int j = i + 1; j < 3; ++j)
-      if (overlaps(outs[i], outb[i], outs[j], outb[j])) return TQ2_ERR_ARG;
-  }
+  if (overlaps(y, yb, partials, pb)) return TQ2_ERR_ARG;
   tq2::MatSet m = {};
   m.codes[0] = codes;
   m.scales[0] = scales;
   m.nmat = 1;
   m.rows = N;
   (void)hipGetLastError();
-  hipError_t e = tq2::launch_i8_stage(x, x_q, K, s, ws, (hipStream_t)stream);
-  if (e != hipSuccess) return TQ2_ERR_HIP;
-  return hip_status(tq2::launch_gemv_i8(m, K, ws, s, y, partials, (hipStream_t)stream));
+  return hip_status(tq2::launch_gemv_i8(m, K, x, x_q, s, y, partials, (hipStream_t)stream));
 }
 
 int32_t tq2_gemv_i8q(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                      const int8_t* x_q, float s, float* y, int32_t* partials, void* ws,
                      size_t ws_bytes, tq2_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
   if (!x_q) return TQ2_ERR_ARG;
-  return i8_common(codes, scales, N, K, nullptr, x_q, s, y, partials, ws, ws_bytes, stream);
+  return i8_common(codes, scales, N, K, nullptr, x_q, s, y, partials, stream);
 }
 
 int32_t tq2_gemv_i8(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                     const uint16_t* x, float s, float* y, void* ws, size_t ws_bytes,
                     tq2_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
   if (!x) return TQ2_ERR_ARG;
-  return i8_common(codes, scales, N, K, x, nullptr, s, y, nullptr, ws, ws_bytes, stream);
+  return i8_common(codes, scales, N, K, x, nullptr, s, y, nullptr, stream);
 }
 
 }  // extern "C"

@@ -23,13 +23,6 @@ struct MatSet {
   int64_t rows;  // total rows over all matrices
 };
 
-// Workspace of the int8 path: permuted x_q (4 KiB per chunk) + per-lane
-// block-sum seeds (256 B per chunk).
-inline size_t i8_workspace_bytes(int64_t K) {
-  size_t b = (size_t)chunks_of(K) * (4096 + 256);
-  return (b + 255) / 256 * 256;
-}
-
 hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* codes,
                        uint16_t* scales, int32_t* bad, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales,
@@ -38,12 +31,10 @@ hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x,
                            float* y, hipStream_t s);
 hipError_t launch_quantize_i8(const uint16_t* x, int64_t K, float scale,
                               int8_t* xq, hipStream_t s);
-// Stage activations for the int8 matvec into `ws`: from fp16 x (quantizing
-// on the way) when x != nullptr, else from pre-quantized xq.
-hipError_t launch_i8_stage(const uint16_t* x, const int8_t* xq, int64_t K,
-                           float scale, void* ws, hipStream_t s);
-hipError_t launch_gemv_i8(const MatSet& m, int64_t K, const void* ws,
-                          float scale, float* y, int32_t* partials,
-                          hipStream_t s);
+// int8 matvec; the activations come either as fp16 x (quantized inside the
+// kernel with scale s) or pre-quantized as xq (exactly one is non-null).
+hipError_t launch_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x,
+                          const int8_t* xq, float s, float* y, int32_t* partials,
+                          hipStream_t st);
 
 }  // namespace tq2

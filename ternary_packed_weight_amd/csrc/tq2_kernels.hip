@@ -152,13 +152,17 @@ hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales,
 
 // ------------------------------------------------------------ fp16 matvec
 //
-// Work split: a wave owns one 4096-wide K-chunk c of R consecutive rows
-// (lane l covers k = 4096c + 64l .. +63, a quarter of one 256-block).  A
-// workgroup holds C chunk-waves for each of S row groups (C = ceil(K/4096),
-// S = max(1, 4/C)), so a row's C partial sums meet in LDS and are added in
-// chunk order: the result is deterministic.  Each wave first issues all its
-// weight loads (R x 16 B per lane), then loads and rearranges its x chunk
-// while they are in flight.
+// Work split.  A wave owns one 4096-wide K-chunk c of R consecutive rows
+// (lane l covers k = 4096c + 64l .. +63: one 16-byte weight load per row, a
+// quarter of one 256-block).  A workgroup holds C = ceil(K/4096) chunk-waves
+// for each of S row groups; a row's C partial sums meet in LDS and are added
+// in chunk order, so the result is deterministic.
+//
+// Order of work in a wave: (1) the workgroup's activation loads and this
+// wave's weight loads are all issued; (2) the activations are staged once
+// per workgroup in LDS, already rearranged for the decode; (3) each wave
+// reads its chunk from LDS (conflict-free, lane-contiguous 16-byte reads),
+// decodes R rows, reduces them across the wave and stores.
 //
 // Decode of one 32-bit code word v (16 weights; byte m holds local weights
 // 4m+j at bits 2j):
@@ -174,54 +178,30 @@ hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales,
 
 constexpr uint32_t kOnesF16x2 = 0x3C003C00u;  // (1.0, 1.0)
 
-// Rearrange a lane's 64 fp16 activations (natural order, 32 dwords) into the
-// decode's operand pairs, and return -(sum of the 64 values) * 2^-24.
-__device__ __forceinline__ float x_pairs_f16(const uint32_t (&xw)[32], uint32_t (&xp)[32]) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t a = xw[8 * g + (j >> 1)], b = xw[8 * g + 4 + (j >> 1)];
-      const uint32_t c = xw[8 * g + 2 + (j >> 1)], d = xw[8 * g + 6 + (j >> 1)];
-      if (j & 1) {
-        xp[8 * g + 2 * j + 0] = (a >> 16) | (b & 0xFFFF0000u);
-        xp[8 * g + 2 * j + 1] = (c >> 16) | (d & 0xFFFF0000u);
-      } else {
-        xp[8 * g + 2 * j + 0] = (a & 0xFFFFu) | (b << 16);
-        xp[8 * g + 2 * j + 1] = (c & 0xFFFFu) | (d << 16);
-      }
-    }
-  }
-  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    s0 = dot2(xw[i + 0], kOnesF16x2, s0);
-    s1 = dot2(xw[i + 1], kOnesF16x2, s1);
-    s2 = dot2(xw[i + 2], kOnesF16x2, s2);
-    s3 = dot2(xw[i + 3], kOnesF16x2, s3);
-  }
-  return -ldexpf((s0 + s1) + (s2 + s3), -24);
-}
-
-// sum_{64 weights} x * q * 2^-24 + seed, i.e. (lane partial of x(q-1)) * 2^-24
+// 64 * (lane partial of x(q-1)) * 2^-24, given seed = -(lane x sum) * 2^-24.
+// Field j contributes sum x q 4^j 2^-24; a Horner chain through one
+// accumulator, h = ((S0 + seed) * 4 + S1) * 4 + S2) * 4 + S3, weights field j
+// by 4^(3-j) with exact power-of-two products, which is 64 times the wanted
+// sum (S0 + seed) + S1/4 + S2/16 + S3/64.  The factor 64 is removed at the
+// end, together with the 2^-24.
 __device__ __forceinline__ float lane_dot_f16(const uint4 w, const uint32_t (&xp)[32],
                                               float seed) {
-  float a0 = seed, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+  uint32_t v8[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const uint32_t v = ws[g], v8 = v >> 8;
-    a0 = dot2(xp[8 * g + 0], v & 0x00030003u, a0);
-    a0 = dot2(xp[8 * g + 1], v8 & 0x00030003u, a0);
-    a1 = dot2(xp[8 * g + 2], v & 0x000C000Cu, a1);
-    a1 = dot2(xp[8 * g + 3], v8 & 0x000C000Cu, a1);
-    a2 = dot2(xp[8 * g + 4], v & 0x00300030u, a2);
-    a2 = dot2(xp[8 * g + 5], v8 & 0x00300030u, a2);
-    a3 = dot2(xp[8 * g + 6], v & 0x00C000C0u, a3);
-    a3 = dot2(xp[8 * g + 7], v8 & 0x00C000C0u, a3);
+  for (int g = 0; g < 4; ++g) v8[g] = v[g] >> 8;
+  float h = seed;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j) h *= 4.0f;
+    const uint32_t mask = 0x00030003u << (2 * j);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      h = dot2(xp[8 * g + 2 * j + 0], v[g] & mask, h);
+      h = dot2(xp[8 * g + 2 * j + 1], v8[g] & mask, h);
+    }
   }
-  // field j sits 2j bits up, so accumulator j carries a factor 4^j: undo it
-  return fmaf(a3, 0.015625f, fmaf(a2, 0.0625f, fmaf(a1, 0.25f, a0)));
+  return h;
 }
 
 // ---- wave64 reduction of R per-lane values (one per row) ----
@@ -231,6 +211,7 @@ __device__ __forceinline__ float lane_dot_f16(const uint4 w, const uint32_t (&xp
 // 16-lane row rho (lanes 16rho..16rho+15, all equal) is the full sum of row
 //   i + (rho & 1) * (R/4) + (rho >> 1) * (R/2)     for R >= 4,
 //   rho >> 1                                         for R == 2.
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
@@ -260,8 +241,11 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 template <int R>
-__device__ __forceinline__ void reduce_rows_f32(float (&v)[R], float (&out)[R >= 4 ? R / 4 : 1]) {
-  static_assert(R == 2 || R == 4 || R == 8, "R must be 2, 4 or 8");
+constexpr int kOut = R >= 4 ? R / 4 : 1;
+
+template <int R>
+__device__ __forceinline__ void reduce_rows_f32(float (&v)[R], float (&out)[kOut<R>]) {
+  static_assert(R == 2 || R == 4 || R == 8 || R == 16, "R must be 2, 4, 8 or 16");
   constexpr int H = R / 2;
 #pragma unroll
   for (int i = 0; i < H; ++i) {
@@ -284,9 +268,11 @@ __device__ __forceinline__ void reduce_rows_f32(float (&v)[R], float (&out)[R >=
   }
 }
 
+// Row of the value out[i] held by 16-lane row rho; -1 if that 16-lane row
+// repeats another one (R == 2).
 template <int R>
 __device__ __forceinline__ int reduced_row(int i, int rho) {
-  if constexpr (R == 2) return rho >> 1;
+  if constexpr (R == 2) return (rho & 1) ? -1 : rho >> 1;
   else return i + (rho & 1) * (R / 4) + (rho >> 1) * (R / 2);
 }
 
@@ -318,90 +304,176 @@ __device__ __forceinline__ RowPtr row_ptr(const MatSet& ms, int64_t row, int64_t
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-// Weights are read exactly once: stream them past the caches.
-__device__ __forceinline__ uint4 load_codes(const uint8_t* p) {
-  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
+// Buffer resource over `bytes` bytes at `base` (raw, untyped access; reads
+// past `bytes` return 0).  Built in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+constexpr int kNonTemporal = 2;  // cache policy: streaming, read once
+
+// One wave's weight words and block-scale bits for R rows.  Every load is
+// unconditional and in bounds (rows past the end read the last row, lanes
+// past K read k = 0) so that nothing waits on a branch; such rows and lanes
+// are zeroed later.  Each load is a raw buffer load: scalar descriptor for
+// the row, 32-bit lane offset, so there is no per-row vector address work.
+template <int R>
+__device__ __forceinline__ void load_rows(const MatSet& ms, int64_t row0, int64_t kk,
+                                          int64_t row_bytes, int64_t BK, uint4 (&w)[R],
+                                          uint16_t (&hs)[R]) {
+  const uint32_t coff = (uint32_t)(kk / 4);                // byte offset in a code row
+  const uint32_t soff = (uint32_t)(kk / kBlock) * 2u;      // byte offset in a scale row
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r < ms.rows ? row0 + r : ms.rows - 1;
+    const RowPtr rp = row_ptr(ms, row, row_bytes, BK);
+    const v4u t = __builtin_bit_cast(
+        v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc(rp.codes, (uint32_t)row_bytes), (int)coff, 0,
+                                                   kNonTemporal));
+    w[r] = make_uint4(t.x, t.y, t.z, t.w);
+    hs[r] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc(rp.scales, (uint32_t)(BK * 2)),
+                                                           (int)soff, 0, 0);
+  }
+}
+
+// Scale bits with padding rows and lanes forced to +0 by masking (a select
+// would let the compiler sink the scale load into a branch).
+__device__ __forceinline__ uint16_t keep_scale(uint16_t h, bool valid) {
+  return (uint16_t)(h & (0u - (uint32_t)valid));
+}
+
+struct Split {
+  int C;  // chunk-waves per row group
+  int S;  // row groups per workgroup
+};
+
+// LDS of the fp16 matvec: x pairs [C][8][64] uint4, group sums [C][64] float4,
+// cross-wave row sums [C*S][R] float.
+__host__ __device__ inline size_t f16_lds_bytes(int C, int S, int R) {
+  return (size_t)C * 8 * 64 * 16 + (size_t)C * 64 * 16 + (size_t)C * S * R * 4;
 }
 
 template <int R, int MAXT>
 __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
                                                    const uint16_t* __restrict__ x,
-                                                   float* __restrict__ y, int C, int S) {
-  __shared__ float red[16][R];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                                                   float* __restrict__ y, Split sp) {
+  extern __shared__ uint4 lds[];
+  const int C = sp.C, S = sp.S;
+  uint4* xpairs = lds;                                          // [C][8][64]
+  float4* gsum = reinterpret_cast<float4*>(lds + C * 8 * 64);   // [C][64]
+  float* red = reinterpret_cast<float*>(gsum + C * 64);         // [C*S][R]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = wave % C;
   const int slot = wave / C;
   const int64_t row0 = ((int64_t)blockIdx.x * S + slot) * R;
   const int64_t k0 = (int64_t)c * kChunk + (int64_t)lane * kLaneK;
   const bool active = k0 < K;
+  const int64_t kk = active ? k0 : 0;
   const int64_t row_bytes = K / 4;
   const int64_t BK = K / kBlock;
+  const int ngroups = (int)(K / 16);  // 16-weight groups to stage
 
-  // 1. every load is unconditional and in bounds (rows past the end read the
-  //    last row, lanes past K read k = 0) so that nothing waits on a branch;
-  //    those lanes and rows are zeroed afterwards through their scale.
-  //    The activations are requested first: memory counters retire in
-  //    order, so x can be rearranged while the weights are still in flight.
-  const int64_t kk = active ? k0 : 0;
-  uint32_t xw[32];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint4 t = *reinterpret_cast<const uint4*>(x + kk + 8 * i);
-    xw[4 * i + 0] = t.x; xw[4 * i + 1] = t.y; xw[4 * i + 2] = t.z; xw[4 * i + 3] = t.w;
+  // (1) loads: one 16-weight group of x per thread (two 16-byte reads,
+  //     coalesced across the workgroup), then this wave's weights.
+  uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+  if (tid < ngroups) {
+    xa = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)tid);
+    xb = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)tid + 8);
   }
   uint4 w[R];
   uint16_t hs[R];
+  load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (2) stage: group m covers weights 16m..16m+15 = group (m % 4) of lane
+  //     (m / 4) % 64 of chunk m / 256.  Its 8 operand pairs go to slots
+  //     2(m%4) and 2(m%4)+1 of that lane; its x sum to gsum[..].(m % 4).
+  //     Groups past K (a partial last chunk) are staged as zeros, so lanes
+  //     beyond K contribute exactly 0.
+  for (int m = tid; m < C * 256; m += blockDim.x) {
+    uint32_t xw[8];
+    if (m >= ngroups) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t row = row0 + r < ms.rows ? row0 + r : ms.rows - 1;
-    const RowPtr rp = row_ptr(ms, row, row_bytes, BK);
-    w[r] = load_codes(rp.codes + kk / 4);
-    hs[r] = rp.scales[kk / kBlock];
+      for (int i = 0; i < 8; ++i) xw[i] = 0;
+    } else if (m == tid) {
+      xw[0] = xa.x; xw[1] = xa.y; xw[2] = xa.z; xw[3] = xa.w;
+      xw[4] = xb.x; xw[5] = xb.y; xw[6] = xb.z; xw[7] = xb.w;
+    } else {
+      const uint4 a2 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)m);
+      const uint4 b2 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)m + 8);
+      xw[0] = a2.x; xw[1] = a2.y; xw[2] = a2.z; xw[3] = a2.w;
+      xw[4] = b2.x; xw[5] = b2.y; xw[6] = b2.z; xw[7] = b2.w;
+    }
+    uint32_t pr[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = xw[j >> 1], b = xw[4 + (j >> 1)];
+      const uint32_t cc = xw[2 + (j >> 1)], d = xw[6 + (j >> 1)];
+      if (j & 1) {
+        pr[2 * j + 0] = (a >> 16) | (b & 0xFFFF0000u);
+        pr[2 * j + 1] = (cc >> 16) | (d & 0xFFFF0000u);
+      } else {
+        pr[2 * j + 0] = (a & 0xFFFFu) | (b << 16);
+        pr[2 * j + 1] = (cc & 0xFFFFu) | (d << 16);
+      }
+    }
+    float s0 = dot2(xw[0], kOnesF16x2, 0.0f), s1 = dot2(xw[1], kOnesF16x2, 0.0f);
+    s0 = dot2(xw[2], kOnesF16x2, s0); s1 = dot2(xw[3], kOnesF16x2, s1);
+    s0 = dot2(xw[4], kOnesF16x2, s0); s1 = dot2(xw[5], kOnesF16x2, s1);
+    s0 = dot2(xw[6], kOnesF16x2, s0); s1 = dot2(xw[7], kOnesF16x2, s1);
+    const int ch = m >> 8, ln = (m >> 2) & 63, gg = m & 3;
+    xpairs[(ch * 8 + 2 * gg) * 64 + ln] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+    xpairs[(ch * 8 + 2 * gg + 1) * 64 + ln] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+    reinterpret_cast<float*>(gsum)[(ch * 64 + ln) * 4 + gg] = s0 + s1;
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the math
-  // 2. rearrange this lane's 64 activations into the decode's operand pairs
+  __syncthreads();
+
+  // (3) this lane's operand pairs and seed -(sum of its 64 x) * 2^-24
   uint32_t xp[32];
-  const float seed = x_pairs_f16(xw, xp);
-  // 3. decode, block partial times its scale
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 tt = xpairs[(c * 8 + i) * 64 + lane];
+    xp[4 * i + 0] = tt.x; xp[4 * i + 1] = tt.y; xp[4 * i + 2] = tt.z; xp[4 * i + 3] = tt.w;
+  }
+  const float4 gs = gsum[c * 64 + lane];
+  const float seed = -ldexpf((gs.x + gs.y) + (gs.z + gs.w), -24);
+
+  // lanes past K hold x = 0 and seed 0, so only padding rows need zeroing
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    // binary16 +0 for padding lanes and rows, by masking the bits (a select
-    // here would let the compiler sink the scale load into a branch)
-    const uint32_t keep = 0u - (uint32_t)(active && row0 + r < ms.rows);
-    const float d = half_to_float((uint16_t)(hs[r] & keep));
+    const float d = half_to_float(keep_scale(hs[r], row0 + r < ms.rows));
     acc[r] = d * lane_dot_f16(w[r], xp, seed);
   }
-  // 4. reduce over the wave
-  float out[R >= 4 ? R / 4 : 1];
+  float out[kOut<R>];
   reduce_rows_f32<R>(acc, out);
   const int rho = lane >> 4;
-  constexpr int NOUT = R >= 4 ? R / 4 : 1;
   if (C == 1) {
     if ((lane & 15) == 0) {
 #pragma unroll
-      for (int i = 0; i < NOUT; ++i) {
-        const int64_t row = row0 + reduced_row<R>(i, rho);
-        if (R != 2 || (rho & 1) == 0)
-          if (row < ms.rows) y[row] = ldexpf(out[i], 24);
+      for (int i = 0; i < kOut<R>; ++i) {
+        const int rr = reduced_row<R>(i, rho);
+        if (rr >= 0 && row0 + rr < ms.rows) y[row0 + rr] = ldexpf(out[i], 18);
       }
     }
     return;
   }
-  // 5. several chunk-waves per row: add their sums in chunk order
+  // several chunk-waves per row: add their sums in chunk order
   if ((lane & 15) == 0) {
 #pragma unroll
-    for (int i = 0; i < NOUT; ++i)
-      if (R != 2 || (rho & 1) == 0) red[wave][reduced_row<R>(i, rho)] = out[i];
+    for (int i = 0; i < kOut<R>; ++i) {
+      const int rr = reduced_row<R>(i, rho);
+      if (rr >= 0) red[wave * R + rr] = out[i];
+    }
   }
   __syncthreads();
   if (c == 0 && lane < R) {
-    float t = red[wave][lane];
-    for (int cc = 1; cc < C; ++cc) t += red[wave + cc][lane];
-    const int64_t row = row0 + lane;
-    if (row < ms.rows) y[row] = ldexpf(t, 24);
+    float tsum = red[wave * R + lane];
+    for (int cc = 1; cc < C; ++cc) tsum += red[(wave + cc) * R + lane];
+    if (row0 + lane < ms.rows) y[row0 + lane] = ldexpf(tsum, 18);
   }
 }
 
@@ -413,33 +485,54 @@ static int device_cus() {
   return cus;
 }
 
-// Rows per wave: as many as keep at least ~8 waves per CU busy (all weight
-// bytes are then in flight at once), at most 8.
-static int pick_rows_per_wave(int64_t rows, int C) {
-  const int64_t want_waves = (int64_t)device_cus() * 8;
-  for (int R : {8, 4}) {
+// Waves per workgroup: C chunk-waves for each of S row groups, 8 waves when
+// C divides 8.
+static Split pick_split(int64_t K) {
+  const int C = (int)chunks_of(K);
+  Split sp;
+  sp.C = C;
+  sp.S = C >= 8 ? 1 : 8 / C;
+  return sp;
+}
+
+// Rows per wave (measured on MI355X): the fp16 matvec does best with ~16
+// waves per CU; the int8 matvec re-quantizes x in every workgroup, so it
+// takes more rows per wave (~8 waves per CU) to have fewer workgroups.
+static int pick_rows_per_wave(int64_t rows, int C, int waves_per_cu, int rmax) {
+  const int64_t want_waves = (int64_t)device_cus() * waves_per_cu;
+  for (int R = rmax; R > 2; R /= 2) {
     if ((rows + R - 1) / R * C >= want_waves) return R;
   }
   return 2;
 }
 
+static hipError_t set_lds_cap(const void* fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+}
+
 template <int R>
 static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
                                hipStream_t s) {
-  const int C = (int)chunks_of(K);
-  const int S = C >= 4 ? 1 : 4 / C;
+  const Split sp = pick_split(K);
   const int64_t groups = (m.rows + R - 1) / R;
-  const int64_t grid = (groups + S - 1) / S;
-  if (C * S <= 4)
-    hipLaunchKernelGGL((k_gemv_f16<R, 256>), dim3((unsigned)grid), dim3(64 * C * S), 0, s, m, K, x, y, C, S);
-  else
-    hipLaunchKernelGGL((k_gemv_f16<R, 1024>), dim3((unsigned)grid), dim3(64 * C * S), 0, s, m, K, x, y, C, S);
+  const int64_t grid = (groups + sp.S - 1) / sp.S;
+  const size_t lds = f16_lds_bytes(sp.C, sp.S, R);
+  const int threads = 64 * sp.C * sp.S;
+  if (threads <= 512) {
+    hipLaunchKernelGGL((k_gemv_f16<R, 512>), dim3((unsigned)grid), dim3(threads), lds, s, m, K, x, y, sp);
+  } else {
+    if (lds > 64 * 1024) {
+      const hipError_t e = set_lds_cap(reinterpret_cast<const void*>(&k_gemv_f16<R, 1024>));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_gemv_f16<R, 1024>), dim3((unsigned)grid), dim3(threads), lds, s, m, K, x, y, sp);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
                            hipStream_t s) {
-  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K))) {
+  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 16, 8)) {
     case 8: return run_gemv_f16<8>(m, K, x, y, s);
     case 4: return run_gemv_f16<4>(m, K, x, y, s);
     default: return run_gemv_f16<2>(m, K, x, y, s);
@@ -448,11 +541,23 @@ hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float*
 
 // ------------------------------------------------------------ int8 path
 // Static int8 activation quantization (page "gemma4 wNa8o8 requires int8
-// activations"): x_q = clamp(rint(x / s), -128, 127), x/s one IEEE fp32
-// division (HIP's default division is correctly rounded), ties to even.
-
-__device__ __forceinline__ int quantize_one(uint16_t xh, float s) {
-  float r = __builtin_rintf(half_to_float(xh) / s);
+// activations"): x_q = clamp(rint(x / s), -128, 127) with x/s one IEEE fp32
+// division and ties to even.
+//
+// Fast exact evaluation: with rs = RN(1/s) and v = RN(x * rs), v lies within
+// 3u|x/s| of RN(x/s) (u = 2^-24).  rint only changes value at half-integers,
+// so when |v| is farther than 8u|v| from the nearest half-integer, rint(v)
+// equals rint(RN(x/s)); otherwise (near a tie, or v not finite) the IEEE
+// division is evaluated.  Saturation at +-127.5/-128.5 gives the same clamped
+// value on either side, so it needs no special case.
+__device__ __forceinline__ int quantize_one(uint16_t xh, float s, float rs) {
+  const float xf = half_to_float(xh);
+  const float v = xf * rs;
+  const float a = fabsf(v);
+  const float frac = a - floorf(a);  // exact: Sterbenz, or a < 1
+  float r;
+  if (fabsf(frac - 0.5f) > a * 0x1p-21f) r = __builtin_rintf(v);
+  else r = __builtin_rintf(xf / s);
   if (__builtin_isnan(r)) r = 0.0f;
   r = fminf(fmaxf(r, -128.0f), 127.0f);
   return (int)r;
@@ -461,7 +566,8 @@ __device__ __forceinline__ int quantize_one(uint16_t xh, float s) {
 __global__ __launch_bounds__(256) void k_quantize_i8(const uint16_t* __restrict__ x, int64_t K,
                                                      float s, int8_t* __restrict__ xq) {
   const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (k < K) xq[k] = (int8_t)quantize_one(x[k], s);
+  const float rs = 1.0f / s;
+  if (k < K) xq[k] = (int8_t)quantize_one(x[k], s, rs);
 }
 
 hipError_t launch_quantize_i8(const uint16_t* x, int64_t K, float scale, int8_t* xq,
@@ -471,72 +577,9 @@ hipError_t launch_quantize_i8(const uint16_t* x, int64_t K, float scale, int8_t*
   return hipGetLastError();
 }
 
-// Staged int8 activations for one lane-chunk (64 weights): 4 uint4 slots,
-// slot g holding dwords j=0..3 = bytes (x_q[16g+j], x_q[16g+4+j],
-// x_q[16g+8+j], x_q[16g+12+j]), the byte order that (v >> 2j) & 0x03030303
-// produces from a code word; plus an int32 seed -(sum of the 64 x_q).
-// Workspace layout: slots [chunks][4][64] uint4, then seeds [chunks][64].
-
-__global__ __launch_bounds__(256) void k_i8_stage(const uint16_t* __restrict__ x,
-                                                  const int8_t* __restrict__ xq_in,
-                                                  int64_t K, float s, uint4* __restrict__ slots,
-                                                  int32_t* __restrict__ seeds) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= K / kLaneK) return;
-  const int64_t c = idx >> 6;
-  const int lane = (int)(idx & 63);
-  int v[64];
-  if (x) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + idx * kLaneK);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 t = src[i];
-      const uint32_t ww[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        v[8 * i + 2 * h] = quantize_one((uint16_t)(ww[h] & 0xFFFFu), s);
-        v[8 * i + 2 * h + 1] = quantize_one((uint16_t)(ww[h] >> 16), s);
-      }
-    }
-  } else {
-    const uint4* src = reinterpret_cast<const uint4*>(xq_in + idx * kLaneK);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 t = src[i];
-      const uint32_t ww[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) v[16 * i + 4 * h + b] = (int)(int8_t)((ww[h] >> (8 * b)) & 0xFFu);
-    }
-  }
-  int sum = 0;
-#pragma unroll
-  for (int t = 0; t < 64; ++t) sum += v[t];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    uint32_t d[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      d[j] = ((uint32_t)(v[16 * g + j] & 0xFF)) | ((uint32_t)(v[16 * g + 4 + j] & 0xFF) << 8) |
-             ((uint32_t)(v[16 * g + 8 + j] & 0xFF) << 16) | ((uint32_t)(v[16 * g + 12 + j] & 0xFF) << 24);
-    slots[(c * 4 + g) * 64 + lane] = make_uint4(d[0], d[1], d[2], d[3]);
-  }
-  seeds[c * 64 + lane] = -sum;
-}
-
-hipError_t launch_i8_stage(const uint16_t* x, const int8_t* xq, int64_t K, float scale,
-                           void* ws, hipStream_t s) {
-  const int64_t chunks = chunks_of(K);
-  uint4* slots = reinterpret_cast<uint4*>(ws);
-  int32_t* seeds = reinterpret_cast<int32_t*>(slots + chunks * 4 * 64);
-  const int64_t n = K / kLaneK;
-  hipLaunchKernelGGL(k_i8_stage, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     x, xq, K, scale, slots, seeds);
-  return hipGetLastError();
-}
-
 // Exact lane partial sum_{64 weights} x_q (q-1), from one 16-byte code load.
+// xq[4g+j] holds bytes (x_q[16g+j], x_q[16g+4+j], x_q[16g+8+j], x_q[16g+12+j]),
+// the order in which (v >> 2j) & 0x03030303 lays out a code word's fields.
 __device__ __forceinline__ int lane_dot_i8(const uint4 w, const uint32_t (&xq)[16], int seed) {
   int a = seed, b = 0, c = 0;
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -597,8 +640,8 @@ __device__ __forceinline__ int64_t row16_sum_i64(int64_t v) {
 }
 
 template <int R>
-__device__ __forceinline__ void reduce_rows_i64(int64_t (&v)[R], int64_t (&out)[R >= 4 ? R / 4 : 1]) {
-  static_assert(R == 2 || R == 4 || R == 8, "R must be 2, 4 or 8");
+__device__ __forceinline__ void reduce_rows_i64(int64_t (&v)[R], int64_t (&out)[kOut<R>]) {
+  static_assert(R == 2 || R == 4 || R == 8 || R == 16, "R must be 2, 4, 8 or 16");
   constexpr int H = R / 2;
 #pragma unroll
   for (int i = 0; i < H; ++i) {
@@ -630,54 +673,109 @@ __device__ __forceinline__ float i8_epilogue(int64_t A, float s) {
   return (float)((a * (double)s) * 0x1p-24);
 }
 
-// Same work split as the fp16 matvec.  Activations come pre-arranged from the
-// staging kernel (4 x 16 B + one seed per lane and chunk), so a wave needs no
-// permutation.  Partials are exact, the cross-wave sum is exact, hence the
-// output does not depend on the reduction order at all.
-template <int R, bool PARTIALS, int MAXT>
+// LDS of the int8 matvec: x_q dwords [C][4][64] uint4, cross-wave sums
+// [C*S][R] int64.
+__host__ __device__ inline size_t i8_lds_bytes(int C, int S, int R) {
+  return (size_t)C * 4 * 64 * 16 + (size_t)C * S * R * 8;
+}
+
+// Same work split as the fp16 matvec.  The workgroup quantizes the
+// activations itself (QUANT: from fp16 x with scale s) or takes them
+// pre-quantized, and stages them in LDS in the dword order of lane_dot_i8.
+// Partials are exact and so is the cross-wave sum: the output does not depend
+// on the reduction order at all.
+template <int R, bool QUANT, bool PARTIALS, int MAXT>
 __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
-                                                  const uint4* __restrict__ slots,
-                                                  const int32_t* __restrict__ seeds, float s,
+                                                  const uint16_t* __restrict__ x,
+                                                  const int8_t* __restrict__ xq_in, float s,
                                                   float* __restrict__ y,
-                                                  int32_t* __restrict__ partials, int C, int S) {
-  __shared__ int64_t red[16][R];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                                                  int32_t* __restrict__ partials, Split sp) {
+  extern __shared__ uint4 lds[];
+  const int C = sp.C, S = sp.S;
+  uint4* xs = lds;                                            // [C][4][64]
+  int64_t* red = reinterpret_cast<int64_t*>(lds + C * 4 * 64);  // [C*S][R]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = wave % C;
   const int slot = wave / C;
   const int64_t row0 = ((int64_t)blockIdx.x * S + slot) * R;
   const int64_t k0 = (int64_t)c * kChunk + (int64_t)lane * kLaneK;
   const bool active = k0 < K;
+  const int64_t kk = active ? k0 : 0;
   const int64_t row_bytes = K / 4;
   const int64_t BK = K / kBlock;
+  const int ngroups = (int)(K / 16);
 
-  // unconditional in-bounds loads, masked afterwards (see the fp16 matvec)
-  const int64_t kk = active ? k0 : 0;
-  uint32_t xq[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 t = slots[((int64_t)c * 4 + i) * 64 + lane];
-    xq[4 * i + 0] = t.x; xq[4 * i + 1] = t.y; xq[4 * i + 2] = t.z; xq[4 * i + 3] = t.w;
+  // (1) loads: first pass of the activations (16 per thread), then weights
+  uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+  if (tid < ngroups) {
+    if (QUANT) {
+      xa = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)tid);
+      xb = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)tid + 8);
+    } else {
+      xa = *reinterpret_cast<const uint4*>(xq_in + 16 * (int64_t)tid);
+    }
   }
-  const int seed = seeds[(int64_t)c * 64 + lane];
   uint4 w[R];
   uint16_t hs[R];
+  load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (2) stage: group m (weights 16m..16m+15) = group m % 4 of lane
+  //     (m / 4) % 64 of chunk m / 256
+  const float rs = 1.0f / s;
+  for (int m = tid; m < ngroups; m += blockDim.x) {
+    uint4 a4 = xa, b4 = xb;
+    if (m != tid) {
+      if (QUANT) {
+        a4 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)m);
+        b4 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)m + 8);
+      } else {
+        a4 = *reinterpret_cast<const uint4*>(xq_in + 16 * (int64_t)m);
+      }
+    }
+    int v[16];
+    if (QUANT) {
+      const uint32_t hw[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t row = row0 + r < ms.rows ? row0 + r : ms.rows - 1;
-    const RowPtr rp = row_ptr(ms, row, row_bytes, BK);
-    w[r] = load_codes(rp.codes + kk / 4);
-    hs[r] = rp.scales[kk / kBlock];
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = quantize_one((uint16_t)(hw[i] & 0xFFFFu), s, rs);
+        v[2 * i + 1] = quantize_one((uint16_t)(hw[i] >> 16), s, rs);
+      }
+    } else {
+      const uint32_t bw[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (int)(int8_t)((bw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    }
+    uint32_t dw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dw[j] = ((uint32_t)v[j] & 0xFFu) | (((uint32_t)v[4 + j] & 0xFFu) << 8) |
+              (((uint32_t)v[8 + j] & 0xFFu) << 16) | (((uint32_t)v[12 + j] & 0xFFu) << 24);
+    const int ch = m >> 8, ln = (m >> 2) & 63, gg = m & 3;
+    xs[(ch * 4 + gg) * 64 + ln] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the math
+  __syncthreads();
+
+  // (3) this lane's activations and seed -(sum of its 64 x_q)
+  uint32_t xq[16];
+  int seed = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 tt = xs[(c * 4 + i) * 64 + lane];
+    xq[4 * i + 0] = tt.x; xq[4 * i + 1] = tt.y; xq[4 * i + 2] = tt.z; xq[4 * i + 3] = tt.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) seed = dot4(xq[i], 0x01010101u, seed);
+  seed = -seed;
 
   int64_t acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int P = lane_dot_i8(w[r], xq, seed);
-    const uint32_t keep = 0u - (uint32_t)(active && row0 + r < ms.rows);
-    const uint16_t h = (uint16_t)(hs[r] & keep);
-    acc[r] = scaled_partial(h, P);
+    acc[r] = scaled_partial(keep_scale(hs[r], active && row0 + r < ms.rows), P);
     if (PARTIALS) {
       // a 256-block spans lanes 4i..4i+3 of this chunk
       int bp = P + __shfl_xor(P, 1, 64);
@@ -686,64 +784,70 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
       if (active && (lane & 3) == 0 && row < ms.rows) partials[row * BK + k0 / kBlock] = bp;
     }
   }
-  int64_t out[R >= 4 ? R / 4 : 1];
+  int64_t out[kOut<R>];
   reduce_rows_i64<R>(acc, out);
   const int rho = lane >> 4;
-  constexpr int NOUT = R >= 4 ? R / 4 : 1;
   if (C == 1) {
     if ((lane & 15) == 0) {
 #pragma unroll
-      for (int i = 0; i < NOUT; ++i) {
-        const int64_t row = row0 + reduced_row<R>(i, rho);
-        if (R != 2 || (rho & 1) == 0)
-          if (row < ms.rows) y[row] = i8_epilogue(out[i], s);
+      for (int i = 0; i < kOut<R>; ++i) {
+        const int rr = reduced_row<R>(i, rho);
+        if (rr >= 0 && row0 + rr < ms.rows) y[row0 + rr] = i8_epilogue(out[i], s);
       }
     }
     return;
   }
   if ((lane & 15) == 0) {
 #pragma unroll
-    for (int i = 0; i < NOUT; ++i)
-      if (R != 2 || (rho & 1) == 0) red[wave][reduced_row<R>(i, rho)] = out[i];
+    for (int i = 0; i < kOut<R>; ++i) {
+      const int rr = reduced_row<R>(i, rho);
+      if (rr >= 0) red[wave * R + rr] = out[i];
+    }
   }
   __syncthreads();
   if (c == 0 && lane < R) {
-    int64_t t = red[wave][lane];
-    for (int cc = 1; cc < C; ++cc) t += red[wave + cc][lane];
-    const int64_t row = row0 + lane;
-    if (row < ms.rows) y[row] = i8_epilogue(t, s);
+    int64_t tsum = red[wave * R + lane];
+    for (int cc = 1; cc < C; ++cc) tsum += red[(wave + cc) * R + lane];
+    if (row0 + lane < ms.rows) y[row0 + lane] = i8_epilogue(tsum, s);
   }
 }
 
-template <int R, bool PARTIALS>
-static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const void* ws, float s, float* y,
-                              int32_t* partials, hipStream_t st) {
-  const int C = (int)chunks_of(K);
-  const int S = C >= 4 ? 1 : 4 / C;
-  const uint4* slots = reinterpret_cast<const uint4*>(ws);
-  const int32_t* seeds = reinterpret_cast<const int32_t*>(slots + (int64_t)C * 4 * 64);
+template <int R, bool QUANT, bool PARTIALS>
+static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
+                              float s, float* y, int32_t* partials, hipStream_t st) {
+  const Split sp = pick_split(K);
   const int64_t groups = (m.rows + R - 1) / R;
-  const int64_t grid = (groups + S - 1) / S;
-  if (C * S <= 4)
-    hipLaunchKernelGGL((k_gemv_i8<R, PARTIALS, 256>), dim3((unsigned)grid), dim3(64 * C * S), 0, st,
-                       m, K, slots, seeds, s, y, partials, C, S);
+  const int64_t grid = (groups + sp.S - 1) / sp.S;
+  const size_t lds = i8_lds_bytes(sp.C, sp.S, R);
+  const int threads = 64 * sp.C * sp.S;
+  if (threads <= 512)
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 512>), dim3((unsigned)grid), dim3(threads), lds,
+                       st, m, K, x, xq, s, y, partials, sp);
   else
-    hipLaunchKernelGGL((k_gemv_i8<R, PARTIALS, 1024>), dim3((unsigned)grid), dim3(64 * C * S), 0, st,
-                       m, K, slots, seeds, s, y, partials, C, S);
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 1024>), dim3((unsigned)grid), dim3(threads), lds,
+                       st, m, K, x, xq, s, y, partials, sp);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_i8(const MatSet& m, int64_t K, const void* ws, float scale, float* y,
-                          int32_t* partials, hipStream_t s) {
-  const int R = pick_rows_per_wave(m.rows, (int)chunks_of(K));
-  if (partials) {
-    if (R == 8) return run_gemv_i8<8, true>(m, K, ws, scale, y, partials, s);
-    if (R == 4) return run_gemv_i8<4, true>(m, K, ws, scale, y, partials, s);
-    return run_gemv_i8<2, true>(m, K, ws, scale, y, partials, s);
+template <int R>
+static hipError_t run_gemv_i8_r(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
+                                float s, float* y, int32_t* partials, hipStream_t st) {
+  if (x) {
+    if (partials) return run_gemv_i8<R, true, true>(m, K, x, xq, s, y, partials, st);
+    return run_gemv_i8<R, true, false>(m, K, x, xq, s, y, partials, st);
   }
-  if (R == 8) return run_gemv_i8<8, false>(m, K, ws, scale, y, partials, s);
-  if (R == 4) return run_gemv_i8<4, false>(m, K, ws, scale, y, partials, s);
-  return run_gemv_i8<2, false>(m, K, ws, scale, y, partials, s);
+  if (partials) return run_gemv_i8<R, false, true>(m, K, x, xq, s, y, partials, st);
+  return run_gemv_i8<R, false, false>(m, K, x, xq, s, y, partials, st);
+}
+
+hipError_t launch_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
+                          float s, float* y, int32_t* partials, hipStream_t st) {
+  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 8, 16)) {
+    case 16: return run_gemv_i8_r<16>(m, K, x, xq, s, y, partials, st);
+    case 8: return run_gemv_i8_r<8>(m, K, x, xq, s, y, partials, st);
+    case 4: return run_gemv_i8_r<4>(m, K, x, xq, s, y, partials, st);
+    default: return run_gemv_i8_r<2>(m, K, x, xq, s, y, partials, st);
+  }
 }
 
 }  // namespace tq2

@@ -53,8 +53,8 @@ def test_sizes(tq2):
     assert tq2.tq2_codes_bytes(1, 100) == 0
     assert tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV, 4096, 4096) == 0
     assert tq2.tq2_workspace_bytes(tq2.TQ2_OP_GATE_UP, 16384, 4096) == 0
-    ws = tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV_I8, 4096, 16384)
-    assert ws >= 16384 + 256 * 4 and ws % 256 == 0
+    assert tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV_I8, 4096, 16384) == 0
+    assert tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV_I8Q, 4096, 65280) == 0
     assert tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV_I8, 4096, 65536) == 2 ** 64 - 1
     assert tq2.tq2_workspace_bytes(99, 1, 256) == 2 ** 64 - 1
     for s in range(7):
@@ -84,7 +84,7 @@ def test_error_paths_gemv(tq2):
     assert g(c=A + 8) == 3 and g(s=A + 2 ** 24 + 1) == 3 and g(x=A + 2 ** 25 + 4) == 3
     assert g(y=A + 2 ** 26 + 2) == 3
     assert g(y=A + 8) == 1                     # y inside codes
-    assert g(y=A + 2 ** 25 - 16) == 1          # y overlapping x... codes plane is 1 KiB
+    assert g(y=A + 2 ** 25 - 16) == 1          # y overlapping x
     gu = lib.tq2_gemv_gate_up(P(A), P(A + 4096), P(0), P(A + 8192), 16, 256, P(A + 2 ** 25),
                               P(A + 2 ** 26), None, 0, None)
     assert gu == 1
@@ -93,25 +93,24 @@ def test_error_paths_gemv(tq2):
 @no_gpu
 def test_error_paths_int8(tq2):
     lib = tq2.lib()
-    ws_need = tq2.tq2_workspace_bytes(tq2.TQ2_OP_GEMV_I8, 16, 256)
 
-    def g(N=16, K=256, s=0.5, ws=A + 2 ** 27, wsb=ws_need, x=A + 2 ** 25, y=A + 2 ** 26):
-        return lib.tq2_gemv_i8(P(A), P(A + 2 ** 24), N, K, P(x), ctypes.c_float(s), P(y), P(ws), wsb, None)
+    def g(N=16, K=256, s=0.5, x=A + 2 ** 25, y=A + 2 ** 26):
+        return lib.tq2_gemv_i8(P(A), P(A + 2 ** 24), N, K, P(x), ctypes.c_float(s), P(y), None, 0, None)
 
-    assert g(K=65280 + 256) == 2
+    assert g(K=65280 + 256) == 2 and g(K=100) == 2 and g(N=0) == 1
     assert g(s=0.0) == 5 and g(s=-1.0) == 5 and g(s=float("inf")) == 5 and g(s=float("nan")) == 5
-    assert g(ws=0) == 4 and g(wsb=ws_need - 1) == 4
-    assert g(ws=A + 2 ** 27 + 128) == 3
-    assert g(ws=A) == 1                        # workspace overlaps codes
-    assert g(x=0) == 1
+    assert g(x=0) == 1 and g(y=0) == 1
+    assert g(x=A + 2 ** 25 + 8) == 3 and g(y=A + 2 ** 26 + 1) == 3
+    assert g(y=A + 64) == 1                    # y inside the code plane
+    assert g(y=A + 2 ** 25 + 256) == 1         # y overlapping x
     q = lib.tq2_gemv_i8q(P(A), P(A + 2 ** 24), 16, 256, P(0), ctypes.c_float(1.0), P(A + 2 ** 26),
-                         None, P(A + 2 ** 27), ws_need, None)
+                         None, None, 0, None)
     assert q == 1
     q = lib.tq2_gemv_i8q(P(A), P(A + 2 ** 24), 16, 256, P(A + 2 ** 25), ctypes.c_float(1.0),
-                         P(A + 2 ** 26), P(A + 2 ** 26 + 2), P(A + 2 ** 27), ws_need, None)
+                         P(A + 2 ** 26), P(A + 2 ** 26 + 2), None, 0, None)
     assert q == 3                              # partials misaligned
     q = lib.tq2_gemv_i8q(P(A), P(A + 2 ** 24), 16, 256, P(A + 2 ** 25), ctypes.c_float(1.0),
-                         P(A + 2 ** 26), P(A + 2 ** 26), P(A + 2 ** 27), ws_need, None)
+                         P(A + 2 ** 26), P(A + 2 ** 26), None, 0, None)
     assert q == 1                              # partials alias y
     assert lib.tq2_quantize_i8(P(A), 256, ctypes.c_float(0.0), P(A + 4096), None) == 5
     assert lib.tq2_quantize_i8(P(A), 255, ctypes.c_float(1.0), P(A + 4096), None) == 2

@@ -249,12 +249,41 @@ def test_quantize_ties_and_clamps(tq2):
         xq = tq2.tq2_quantize_i8(torch.from_numpy(vals).to(DEV), np.float32(s))
         torch.cuda.synchronize()
         assert np.array_equal(xq.cpu().numpy(), oracle.quantize_i8(synth.bits(vals), np.float32(s))), s
-    # every finite binary16 value against the oracle for one scale
+    # every finite binary16 value against the oracle, for scales that put
+    # many quotients exactly on or next to half-integers (powers of two,
+    # thirds, tenths) and for arbitrary ones
     allh = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
     allh = np.where(np.isfinite(allh), allh, np.float16(0)).astype(np.float16)
-    xq = tq2.tq2_quantize_i8(torch.from_numpy(allh).to(DEV), np.float32(0.0371))
-    torch.cuda.synchronize()
-    assert np.array_equal(xq.cpu().numpy(), oracle.quantize_i8(synth.bits(allh), np.float32(0.0371)))
+    xd = torch.from_numpy(allh).to(DEV)
+    scales = [0.0371, 0.5, 1.0 / 3.0, 0.1, 2.0 ** -10, 3.0, 100.0, 1e-3, 7.0 / 1024.0, 65504.0 / 127]
+    scales += list(synth.rng(8).uniform(1e-4, 1.0, 6))
+    for s in scales:
+        s = np.float32(s)
+        xq = tq2.tq2_quantize_i8(xd, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(xq.cpu().numpy(), oracle.quantize_i8(synth.bits(allh), s)), float(s)
+
+
+def test_gemv_i8_fused_quantizer_all_fp16(tq2):
+    """The quantizer inside the fused int8 matvec agrees with the oracle on
+    every finite binary16 activation (K = 65280 covers 63488 of them)."""
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    allh = allh[np.isfinite(allh)][:65280].astype(np.float16)
+    K = allh.size
+    N = 3
+    q, codes, scales, _ = _packed(970, N, K)
+    for s in (np.float32(0.5), np.float32(1.0 / 3.0), np.float32(0.0371)):
+        c, sc, xd = _to_dev(codes, scales, allh)
+        P = torch.empty((N, K // 256), dtype=torch.int32, device=DEV)
+        y = tq2.tq2_gemv_i8(c, sc, xd, s)
+        xq = tq2.tq2_quantize_i8(xd, s)
+        y2 = tq2.tq2_gemv_i8q(c, sc, xq, s, partials=P)
+        torch.cuda.synchronize()
+        xq_ref = oracle.quantize_i8(synth.bits(allh), s)
+        y_ref, P_ref = oracle.gemv_i8q(codes, scales, N, K, xq_ref, s)
+        assert np.array_equal(P.cpu().numpy(), P_ref)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), float(s)
+        assert np.array_equal(y2.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), float(s)
 
 
 I8_SHAPES = [(1, 256, 100), (3, 768, 100), (33, 4096, 200), (257, 4352, 100), (4096, 16384, 100),
