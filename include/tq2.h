@@ -29,7 +29,8 @@
  *     or truncated.  Device faults surface at the caller's synchronization.
  *   - Outputs must not alias inputs.
  *   - K must be a positive multiple of 256 and at most TQ2_MAX_K
- *     (TQ2_I8_MAX_K on the int8 path).  N is any value >= 1, N*K < 2^40.
+ *     (TQ2_I8_MAX_K on the int8 path).  N is any value with
+ *     1 <= N <= TQ2_MAX_ROWS and N*K < 2^40.
  *   - Alignment: codes, x, x_q and W 16 bytes; scales 2; y, partials 4.
  */
 #ifndef TQ2_H
@@ -45,6 +46,7 @@ extern "C" {
 #define TQ2_ABI_VERSION 1
 #define TQ2_BLOCK 256
 #define TQ2_MAX_K 65536    /* fp16 activations staged on chip: 16 x 4096 */
+#define TQ2_MAX_ROWS 1073741823 /* rows of one call (gate+up: both matrices) < 2^31 */
 #define TQ2_I8_MAX_K 65280 /* 255 blocks: keeps the exact int64 sum in range */
 
 enum tq2_status {

@@ -20,7 +20,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 int32_t check_shape(int64_t N, int64_t K, int64_t kmax) {
   if (N < 1) return TQ2_ERR_ARG;
   if (K < TQ2_BLOCK || K % TQ2_BLOCK != 0 || K > kmax) return TQ2_ERR_SHAPE;
-  if (N > ((int64_t)1 << 40) / K) return TQ2_ERR_SHAPE;
+  if (N > TQ2_MAX_ROWS || N > ((int64_t)1 << 40) / K) return TQ2_ERR_SHAPE;
   return TQ2_OK;
 }
 
@@ -128,10 +128,10 @@ static int32_t gemv_common(const uint8_t* const* codes, const uint16_t* const* s
   for (int i = 0; i < nmat; ++i) {
     m.codes[i] = codes[i];
     m.scales[i] = scales[i];
-    m.row_begin[i] = i * N;
+    m.row_begin[i] = (int32_t)(i * N);
   }
   m.nmat = nmat;
-  m.rows = nmat * N;
+  m.rows = (int32_t)(nmat * N);
   (void)hipGetLastError();
   return hip_status(tq2::launch_gemv_f16(m, K, x, y, (hipStream_t)stream));
 }
@@ -188,7 +188,7 @@ static int32_t i8_common(const uint8_t* codes, const uint16_t* scales, int64_t N
   m.codes[0] = codes;
   m.scales[0] = scales;
   m.nmat = 1;
-  m.rows = N;
+  m.rows = (int32_t)N;
   (void)hipGetLastError();
   return hip_status(tq2::launch_gemv_i8(m, K, x, x_q, s, y, partials, (hipStream_t)stream));
 }

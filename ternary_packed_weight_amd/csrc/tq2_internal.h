@@ -15,12 +15,14 @@ __host__ __device__ inline int64_t chunks_of(int64_t K) { return (K + kChunk - 1
 
 // Up to three weight matrices that share K and the activation vector; their
 // outputs are concatenated in y (matrix m, row n -> y[row_begin[m] + n]).
+// Row indices are 32-bit (the ABI limits the total row count to < 2^31), so
+// every wave-uniform row test is a scalar compare.
 struct MatSet {
   const uint8_t* codes[3];
   const uint16_t* scales[3];
-  int64_t row_begin[3];
+  int32_t row_begin[3];
   int32_t nmat;
-  int64_t rows;  // total rows over all matrices
+  int32_t rows;  // total rows over all matrices
 };
 
 hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* codes,

@@ -190,14 +190,16 @@ __device__ __forceinline__ float lane_dot_f16(const uint4 w, const uint32_t (&xp
   uint32_t v8[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) v8[g] = v[g] >> 8;
-  float h = seed;
+  // first product in the three-source form, so the seed needs no copy
+  float h;
+  asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(h) : "v"(xp[0]), "v"(v[0] & 0x00030003u), "v"(seed));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (j) h *= 4.0f;
     const uint32_t mask = 0x00030003u << (2 * j);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      h = dot2(xp[8 * g + 2 * j + 0], v[g] & mask, h);
+      if (j || g) h = dot2(xp[8 * g + 2 * j + 0], v[g] & mask, h);
       h = dot2(xp[8 * g + 2 * j + 1], v8[g] & mask, h);
     }
   }
@@ -284,9 +286,9 @@ struct RowPtr {
   const uint16_t* scales;
 };
 
-__device__ __forceinline__ RowPtr row_ptr(const MatSet& ms, int64_t row, int64_t row_bytes,
+__device__ __forceinline__ RowPtr row_ptr(const MatSet& ms, int row, int64_t row_bytes,
                                           int64_t BK) {
-  int64_t lr = row;
+  int lr = row;
   const uint8_t* c = ms.codes[0];
   const uint16_t* s = ms.scales[0];
   if (ms.nmat > 1 && row >= ms.row_begin[1]) {
@@ -299,7 +301,7 @@ __device__ __forceinline__ RowPtr row_ptr(const MatSet& ms, int64_t row, int64_t
     c = ms.codes[2];
     s = ms.scales[2];
   }
-  return RowPtr{c + lr * row_bytes, s + lr * BK};
+  return RowPtr{c + (int64_t)lr * row_bytes, s + (int64_t)lr * BK};
 }
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -318,14 +320,14 @@ constexpr int kNonTemporal = 2;  // cache policy: streaming, read once
 // are zeroed later.  Each load is a raw buffer load: scalar descriptor for
 // the row, 32-bit lane offset, so there is no per-row vector address work.
 template <int R>
-__device__ __forceinline__ void load_rows(const MatSet& ms, int64_t row0, int64_t kk,
+__device__ __forceinline__ void load_rows(const MatSet& ms, int row0, int64_t kk,
                                           int64_t row_bytes, int64_t BK, uint4 (&w)[R],
                                           uint16_t (&hs)[R]) {
   const uint32_t coff = (uint32_t)(kk / 4);                // byte offset in a code row
   const uint32_t soff = (uint32_t)(kk / kBlock) * 2u;      // byte offset in a scale row
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t row = row0 + r < ms.rows ? row0 + r : ms.rows - 1;
+    const int row = row0 + r < ms.rows ? row0 + r : ms.rows - 1;
     const RowPtr rp = row_ptr(ms, row, row_bytes, BK);
     const v4u t = __builtin_bit_cast(
         v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc(rp.codes, (uint32_t)row_bytes), (int)coff, 0,
@@ -334,12 +336,6 @@ __device__ __forceinline__ void load_rows(const MatSet& ms, int64_t row0, int64_
     hs[r] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc(rp.scales, (uint32_t)(BK * 2)),
                                                            (int)soff, 0, 0);
   }
-}
-
-// Scale bits with padding rows and lanes forced to +0 by masking (a select
-// would let the compiler sink the scale load into a branch).
-__device__ __forceinline__ uint16_t keep_scale(uint16_t h, bool valid) {
-  return (uint16_t)(h & (0u - (uint32_t)valid));
 }
 
 struct Split {
@@ -353,22 +349,25 @@ __host__ __device__ inline size_t f16_lds_bytes(int C, int S, int R) {
   return (size_t)C * 8 * 64 * 16 + (size_t)C * 64 * 16 + (size_t)C * S * R * 4;
 }
 
-template <int R, int MAXT>
+// CT: chunk-waves per row group as a compile-time constant (1, 2, 4), or 0
+// to take it from `sp` at run time.
+template <int R, int CT, int MAXT>
 __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
                                                    const uint16_t* __restrict__ x,
                                                    float* __restrict__ y, Split sp) {
   extern __shared__ uint4 lds[];
-  const int C = sp.C, S = sp.S;
+  const int C = CT ? CT : sp.C, S = sp.S;
   uint4* xpairs = lds;                                          // [C][8][64]
   float4* gsum = reinterpret_cast<float4*>(lds + C * 8 * 64);   // [C][64]
   float* red = reinterpret_cast<float*>(gsum + C * 64);         // [C*S][R]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // wave-uniform indices, kept in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = wave % C;
-  const int slot = wave / C;
-  const int64_t row0 = ((int64_t)blockIdx.x * S + slot) * R;
+  const int slot = __builtin_amdgcn_readfirstlane(wave / C);
+  const int c = wave - slot * C;
+  const int row0 = ((int)blockIdx.x * S + slot) * R;
   const int64_t k0 = (int64_t)c * kChunk + (int64_t)lane * kLaneK;
   const bool active = k0 < K;
   const int64_t kk = active ? k0 : 0;
@@ -377,12 +376,11 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   const int ngroups = (int)(K / 16);  // 16-weight groups to stage
 
   // (1) loads: one 16-weight group of x per thread (two 16-byte reads,
-  //     coalesced across the workgroup), then this wave's weights.
-  uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-  if (tid < ngroups) {
-    xa = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)tid);
-    xb = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)tid + 8);
-  }
+  //     coalesced across the workgroup; clamped, so unconditional), then
+  //     this wave's weights.
+  const int g0 = tid < ngroups ? tid : ngroups - 1;
+  const uint4 xa = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)g0);
+  const uint4 xb = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)g0 + 8);
   uint4 w[R];
   uint16_t hs[R];
   load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs);
@@ -394,19 +392,15 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   //     Groups past K (a partial last chunk) are staged as zeros, so lanes
   //     beyond K contribute exactly 0.
   for (int m = tid; m < C * 256; m += blockDim.x) {
-    uint32_t xw[8];
-    if (m >= ngroups) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xw[i] = 0;
-    } else if (m == tid) {
-      xw[0] = xa.x; xw[1] = xa.y; xw[2] = xa.z; xw[3] = xa.w;
-      xw[4] = xb.x; xw[5] = xb.y; xw[6] = xb.z; xw[7] = xb.w;
-    } else {
-      const uint4 a2 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)m);
-      const uint4 b2 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)m + 8);
-      xw[0] = a2.x; xw[1] = a2.y; xw[2] = a2.z; xw[3] = a2.w;
-      xw[4] = b2.x; xw[5] = b2.y; xw[6] = b2.z; xw[7] = b2.w;
+    uint4 a4 = xa, b4 = xb;
+    if (m != tid) {  // second pass (K > 8 * blockDim): rare
+      const int gm = m < ngroups ? m : ngroups - 1;
+      a4 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm);
+      b4 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm + 8);
     }
+    const uint32_t z = m < ngroups ? 0xFFFFFFFFu : 0u;
+    const uint32_t xw[8] = {a4.x & z, a4.y & z, a4.z & z, a4.w & z,
+                            b4.x & z, b4.y & z, b4.z & z, b4.w & z};
     uint32_t pr[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -441,12 +435,14 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   const float4 gs = gsum[c * 64 + lane];
   const float seed = -ldexpf((gs.x + gs.y) + (gs.z + gs.w), -24);
 
-  // lanes past K hold x = 0 and seed 0, so only padding rows need zeroing
+  // lanes past K hold x = 0 and seed 0, so only padding rows need zeroing;
+  // the row test is wave-uniform (a scalar select of the mask)
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float d = half_to_float(keep_scale(hs[r], row0 + r < ms.rows));
-    acc[r] = d * lane_dot_f16(w[r], xp, seed);
+    const uint32_t keep = row0 + r < ms.rows ? 0xFFFFu : 0u;
+    const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hs[r] & keep));
+    acc[r] = __builtin_fmaf((float)d, lane_dot_f16(w[r], xp, seed), 0.0f);  // v_fma_mix
   }
   float out[kOut<R>];
   reduce_rows_f32<R>(acc, out);
@@ -485,19 +481,19 @@ static int device_cus() {
   return cus;
 }
 
-// Waves per workgroup: C chunk-waves for each of S row groups, 8 waves when
-// C divides 8.
+// Waves per workgroup: C chunk-waves for each of S row groups.  8 waves when
+// C divides 8, except K = 16384 (C = 4), where 16-wave workgroups halve the
+// activation staging per row and measured faster on MI355X.
 static Split pick_split(int64_t K) {
   const int C = (int)chunks_of(K);
   Split sp;
   sp.C = C;
-  sp.S = C >= 8 ? 1 : 8 / C;
+  sp.S = C == 4 ? 4 : (C >= 8 ? 1 : 8 / C);
   return sp;
 }
 
-// Rows per wave (measured on MI355X): the fp16 matvec does best with ~16
-// waves per CU; the int8 matvec re-quantizes x in every workgroup, so it
-// takes more rows per wave (~8 waves per CU) to have fewer workgroups.
+// Rows per wave (measured on MI355X): both matvecs do best with ~16 waves
+// per CU, i.e. as many rows per wave (up to rmax) as still give that many.
 static int pick_rows_per_wave(int64_t rows, int C, int waves_per_cu, int rmax) {
   const int64_t want_waves = (int64_t)device_cus() * waves_per_cu;
   for (int R = rmax; R > 2; R /= 2) {
@@ -515,17 +511,23 @@ static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, fl
                                hipStream_t s) {
   const Split sp = pick_split(K);
   const int64_t groups = (m.rows + R - 1) / R;
-  const int64_t grid = (groups + sp.S - 1) / sp.S;
+  const dim3 grid((unsigned)((groups + sp.S - 1) / sp.S));
   const size_t lds = f16_lds_bytes(sp.C, sp.S, R);
-  const int threads = 64 * sp.C * sp.S;
-  if (threads <= 512) {
-    hipLaunchKernelGGL((k_gemv_f16<R, 512>), dim3((unsigned)grid), dim3(threads), lds, s, m, K, x, y, sp);
+  const dim3 block(64 * sp.C * sp.S);
+  if (sp.C == 1) {
+    hipLaunchKernelGGL((k_gemv_f16<R, 1, 512>), grid, block, lds, s, m, K, x, y, sp);
+  } else if (sp.C == 2) {
+    hipLaunchKernelGGL((k_gemv_f16<R, 2, 512>), grid, block, lds, s, m, K, x, y, sp);
+  } else if (sp.C == 4) {
+    hipLaunchKernelGGL((k_gemv_f16<R, 4, 1024>), grid, block, lds, s, m, K, x, y, sp);
+  } else if (block.x <= 512) {
+    hipLaunchKernelGGL((k_gemv_f16<R, 0, 512>), grid, block, lds, s, m, K, x, y, sp);
   } else {
     if (lds > 64 * 1024) {
-      const hipError_t e = set_lds_cap(reinterpret_cast<const void*>(&k_gemv_f16<R, 1024>));
+      const hipError_t e = set_lds_cap(reinterpret_cast<const void*>(&k_gemv_f16<R, 0, 1024>));
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_gemv_f16<R, 1024>), dim3((unsigned)grid), dim3(threads), lds, s, m, K, x, y, sp);
+    hipLaunchKernelGGL((k_gemv_f16<R, 0, 1024>), grid, block, lds, s, m, K, x, y, sp);
   }
   return hipGetLastError();
 }
@@ -684,23 +686,23 @@ __host__ __device__ inline size_t i8_lds_bytes(int C, int S, int R) {
 // pre-quantized, and stages them in LDS in the dword order of lane_dot_i8.
 // Partials are exact and so is the cross-wave sum: the output does not depend
 // on the reduction order at all.
-template <int R, bool QUANT, bool PARTIALS, int MAXT>
+template <int R, bool QUANT, bool PARTIALS, int CT, int MAXT>
 __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
                                                   const uint16_t* __restrict__ x,
                                                   const int8_t* __restrict__ xq_in, float s,
                                                   float* __restrict__ y,
                                                   int32_t* __restrict__ partials, Split sp) {
   extern __shared__ uint4 lds[];
-  const int C = sp.C, S = sp.S;
+  const int C = CT ? CT : sp.C, S = sp.S;
   uint4* xs = lds;                                            // [C][4][64]
   int64_t* red = reinterpret_cast<int64_t*>(lds + C * 4 * 64);  // [C*S][R]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = wave % C;
-  const int slot = wave / C;
-  const int64_t row0 = ((int64_t)blockIdx.x * S + slot) * R;
+  const int slot = __builtin_amdgcn_readfirstlane(wave / C);
+  const int c = wave - slot * C;
+  const int row0 = ((int)blockIdx.x * S + slot) * R;
   const int64_t k0 = (int64_t)c * kChunk + (int64_t)lane * kLaneK;
   const bool active = k0 < K;
   const int64_t kk = active ? k0 : 0;
@@ -775,13 +777,14 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int P = lane_dot_i8(w[r], xq, seed);
-    acc[r] = scaled_partial(keep_scale(hs[r], active && row0 + r < ms.rows), P);
+    const uint32_t keep = (row0 + r < ms.rows ? 0xFFFFu : 0u) & (0u - (uint32_t)active);
+    acc[r] = scaled_partial((uint16_t)(hs[r] & keep), P);
     if (PARTIALS) {
       // a 256-block spans lanes 4i..4i+3 of this chunk
       int bp = P + __shfl_xor(P, 1, 64);
       bp += __shfl_xor(bp, 2, 64);
-      const int64_t row = row0 + r;
-      if (active && (lane & 3) == 0 && row < ms.rows) partials[row * BK + k0 / kBlock] = bp;
+      const int row = row0 + r;
+      if (active && (lane & 3) == 0 && row < ms.rows) partials[(int64_t)row * BK + k0 / kBlock] = bp;
     }
   }
   int64_t out[kOut<R>];
@@ -820,11 +823,17 @@ static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, con
   const int64_t grid = (groups + sp.S - 1) / sp.S;
   const size_t lds = i8_lds_bytes(sp.C, sp.S, R);
   const int threads = 64 * sp.C * sp.S;
-  if (threads <= 512)
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 512>), dim3((unsigned)grid), dim3(threads), lds,
+  if (sp.C == 1)
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 1, 512>), dim3((unsigned)grid), dim3(threads), lds,
+                       st, m, K, x, xq, s, y, partials, sp);
+  else if (sp.C == 4)
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 4, 1024>), dim3((unsigned)grid), dim3(threads), lds,
+                       st, m, K, x, xq, s, y, partials, sp);
+  else if (threads <= 512)
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 512>), dim3((unsigned)grid), dim3(threads), lds,
                        st, m, K, x, xq, s, y, partials, sp);
   else
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 1024>), dim3((unsigned)grid), dim3(threads), lds,
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 1024>), dim3((unsigned)grid), dim3(threads), lds,
                        st, m, K, x, xq, s, y, partials, sp);
   return hipGetLastError();
 }
@@ -842,8 +851,7 @@ static hipError_t run_gemv_i8_r(const MatSet& m, int64_t K, const uint16_t* x, c
 
 hipError_t launch_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
                           float s, float* y, int32_t* partials, hipStream_t st) {
-  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 8, 16)) {
-    case 16: return run_gemv_i8_r<16>(m, K, x, xq, s, y, partials, st);
+  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 16, 8)) {
     case 8: return run_gemv_i8_r<8>(m, K, x, xq, s, y, partials, st);
     case 4: return run_gemv_i8_r<4>(m, K, x, xq, s, y, partials, st);
     default: return run_gemv_i8_r<2>(m, K, x, xq, s, y, partials, st);
