@@ -155,6 +155,52 @@ int32_t tq2_gemv_i8(const uint8_t *codes, const uint16_t *scales, int64_t N,
                     int64_t K, const uint16_t *x, float s, float *y, void *ws,
                     size_t ws_bytes, tq2_stream_t stream);
 
+/* ---- linears that share one input, and fused epilogues ---- */
+
+/* tq2_gemv_fused -- nmat (1..3) matrices with the same K and row counts
+ * N[0..nmat-1] sharing one fp16 x, in one kernel (page "gemma4 wNa8o8
+ * requires int8 activations": q, k and v share their input, as do gate and
+ * up).  codes/scales/N are HOST arrays of nmat entries (the matrices
+ * themselves are device memory).  y is the concatenation [N0 | N1 | N2] of
+ * the outputs.  Same arithmetic and accuracy as tq2_gemv; the sum of the
+ * N[i] is at most TQ2_MAX_ROWS. */
+int32_t tq2_gemv_fused(int32_t nmat, const uint8_t *const *codes,
+                       const uint16_t *const *scales, const int64_t *N,
+                       int64_t K, const uint16_t *x, float *y, void *ws,
+                       size_t ws_bytes, tq2_stream_t stream);
+
+/* tq2_gemv_i8_fused -- the int8 matvec (tq2_gemv_i8) over nmat (1..3)
+ * matrices sharing one fp16 x and one activation scale s: x is quantized
+ * once per workgroup, as the shared-input rule of the same page allows (the
+ * input scales of q/k/v, and of gate/up, are equal).  Each output is
+ * bit-identical to tq2_gemv_i8 of its matrix.  Arrays as tq2_gemv_fused. */
+int32_t tq2_gemv_i8_fused(int32_t nmat, const uint8_t *const *codes,
+                          const uint16_t *const *scales, const int64_t *N,
+                          int64_t K, const uint16_t *x, float s, float *y,
+                          void *ws, size_t ws_bytes, tq2_stream_t stream);
+
+/* tq2_gemv_gate_up_silu -- h[n] = silu(g[n]) * u[n], silu(v) = v/(1+exp(-v)),
+ * where g and u are the fp16-x matvecs of the gate and up matrices ([N][K]
+ * each) with a shared x: the MLP activation fused into the gate+up kernel
+ * (page "Custom Metal kernels": several graph ops collapsed into one
+ * dispatch).  Only h[N] (fp32) is written.  g and u carry the tq2_gemv
+ * accuracy; the epilogue is fp32 (expf and one IEEE division). */
+int32_t tq2_gemv_gate_up_silu(const uint8_t *codes_g, const uint16_t *scales_g,
+                              const uint8_t *codes_u, const uint16_t *scales_u,
+                              int64_t N, int64_t K, const uint16_t *x, float *h,
+                              void *ws, size_t ws_bytes, tq2_stream_t stream);
+
+/* tq2_gemv_i8_requant -- the whole static-int8 linear of the wNa8o8 page's
+ * recipe: quantize x with s_in, int8 x ternary matvec (y exactly as
+ * tq2_gemv_i8), then requantize the output with the static output scale:
+ * y_q = clamp(rint(y / s_out), -128, 127) (one IEEE fp32 division, ties to
+ * even), and, if y_deq is non-NULL, the dequantized y_deq = y_q * s_out
+ * (fp32).  s_in and s_out must be finite and > 0.  One kernel. */
+int32_t tq2_gemv_i8_requant(const uint8_t *codes, const uint16_t *scales,
+                            int64_t N, int64_t K, const uint16_t *x, float s_in,
+                            float s_out, int8_t *y_q, float *y_deq, void *ws,
+                            size_t ws_bytes, tq2_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

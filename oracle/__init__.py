@@ -12,6 +12,8 @@ Functions (each cites its passage in tq2_oracle.c):
   partials_i8(codes, N, K, x_q) -> P [N][K/256]
   gemv_i8q(codes, scales, N, K, x_q, s) -> y, P
   gemv_i8(codes, scales, N, K, x_bits, s) -> y
+  requant_i8(y, s_out)         -> y_q, y_deq
+  silu_mul(g, u)               -> h (fp64)
   half_to_float(bits), float_to_half(value)
 """
 import ctypes
@@ -50,6 +52,10 @@ def _lib():
         lib.oracle_gemv_i8q.restype = None
         lib.oracle_gemv_i8.argtypes = [P, P, I64, I64, P, ctypes.c_float, P]
         lib.oracle_gemv_i8.restype = None
+        lib.oracle_requant_i8.argtypes = [P, I64, ctypes.c_float, P, P]
+        lib.oracle_requant_i8.restype = None
+        lib.oracle_silu_mul.argtypes = [P, P, I64, P]
+        lib.oracle_silu_mul.restype = None
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         _LIB = lib
@@ -148,3 +154,21 @@ def gemv_i8(codes, scales, N, K, x_bits, s):
     y = np.empty(N, np.float32)
     _lib().oracle_gemv_i8(pc, ps, N, K, px, float(np.float32(s)), y.ctypes.data_as(ctypes.c_void_p))
     return y
+
+
+def requant_i8(y, s_out):
+    y, py = _c(y, np.float32)
+    N = y.size
+    yq = np.empty(N, np.int8)
+    yd = np.empty(N, np.float32)
+    _lib().oracle_requant_i8(py, N, float(np.float32(s_out)), yq.ctypes.data_as(ctypes.c_void_p),
+                             yd.ctypes.data_as(ctypes.c_void_p))
+    return yq, yd
+
+
+def silu_mul(g, u):
+    g, pg = _c(g, np.float32)
+    u, pu = _c(u, np.float32)
+    h = np.empty(g.size, np.float64)
+    _lib().oracle_silu_mul(pg, pu, g.size, h.ctypes.data_as(ctypes.c_void_p))
+    return h

@@ -240,3 +240,31 @@ int oracle_threads(void) { return omp_get_max_threads(); }
 #else
 int oracle_threads(void) { return 1; }
 #endif
+
+/* ---- output requantization (page "gemma4 wNa8o8 requires int8
+ * activations", the recipe paragraph: the int8 matmul's result is
+ * requantized to int8 with the output activation scale, then dequantized).
+ * Readings as for the input quantizer: one IEEE fp32 division, rint (ties to
+ * even), clamp in float; the dequantized value is one fp32 product. */
+void oracle_requant_i8(const float *y, int64_t N, float s_out, int8_t *y_q,
+                       float *y_deq)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        float r = rintf(y[n] / s_out);
+        if (isnan(r)) r = 0.0f;
+        if (r < -128.0f) r = -128.0f;
+        if (r > 127.0f) r = 127.0f;
+        y_q[n] = (int8_t)r;
+        if (y_deq) y_deq[n] = r * s_out;
+    }
+}
+
+/* ---- SiLU(gate) * up in fp64 (reference for the fused MLP epilogue):
+ * silu(v) = v / (1 + e^-v). */
+void oracle_silu_mul(const float *g, const float *u, int64_t N, double *h)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        double v = (double)g[n];
+        h[n] = v / (1.0 + exp(-v)) * (double)u[n];
+    }
+}

@@ -112,27 +112,51 @@ int32_t tq2_dequant(const uint8_t* codes, const uint16_t* scales, int64_t N, int
   return hip_status(tq2::launch_dequant(codes, scales, N, K, W, (hipStream_t)stream));
 }
 
-static int32_t gemv_common(const uint8_t* const* codes, const uint16_t* const* scales, int nmat,
-                           int64_t N, int64_t K, const uint16_t* x, float* y,
-                           tq2_stream_t stream) {
-  TQ2_TRY(check_shape(N, K, TQ2_MAX_K));
-  if (!x || !y) return TQ2_ERR_ARG;
-  for (int i = 0; i < nmat; ++i) TQ2_TRY(check_weights(codes[i], scales[i]));
-  if (!aligned(x, 16) || !aligned(y, 4)) return TQ2_ERR_ALIGN;
-  const size_t yb = (size_t)(nmat * N) * 4;
-  if (overlaps(y, yb, x, (size_t)K * 2)) return TQ2_ERR_ARG;
-  for (int i = 0; i < nmat; ++i)
-    if (overlaps(y, yb, codes[i], (size_t)(N * K / 4)) || overlaps(y, yb, scales[i], (size_t)(N * K / 128)))
-      return TQ2_ERR_ARG;
-  tq2::MatSet m = {};
+// Validate nmat (1..3) matrices of the same K and row counts N[i] sharing x,
+// and describe them as one concatenated row space.
+static int32_t build_matset(int nmat, const uint8_t* const* codes, const uint16_t* const* scales,
+                            const int64_t* N, int64_t K, int64_t kmax, tq2::MatSet* m) {
+  if (nmat < 1 || nmat > 3 || !codes || !scales || !N) return TQ2_ERR_ARG;
+  int64_t total = 0;
+  *m = tq2::MatSet{};
   for (int i = 0; i < nmat; ++i) {
-    m.codes[i] = codes[i];
-    m.scales[i] = scales[i];
-    m.row_begin[i] = (int32_t)(i * N);
+    TQ2_TRY(check_shape(N[i], K, kmax));
+    TQ2_TRY(check_weights(codes[i], scales[i]));
+    m->codes[i] = codes[i];
+    m->scales[i] = scales[i];
+    m->row_begin[i] = (int32_t)total;
+    total += N[i];
   }
-  m.nmat = nmat;
-  m.rows = (int32_t)(nmat * N);
+  if (total > TQ2_MAX_ROWS) return TQ2_ERR_SHAPE;
+  m->nmat = nmat;
+  m->rows = (int32_t)total;
+  return TQ2_OK;
+}
+
+// Outputs must not overlap any input of the call.
+static bool output_clear(const void* out, size_t out_b, const tq2::MatSet& m, int64_t K,
+                         const void* x, size_t x_b) {
+  if (overlaps(out, out_b, x, x_b)) return false;
+  for (int i = 0; i < m.nmat; ++i) {
+    const int64_t n = (i + 1 < m.nmat ? m.row_begin[i + 1] : m.rows) - m.row_begin[i];
+    if (overlaps(out, out_b, m.codes[i], (size_t)(n * K / 4)) ||
+        overlaps(out, out_b, m.scales[i], (size_t)(n * K / 128)))
+      return false;
+  }
+  return true;
+}
+
+static int32_t gemv_common(int nmat, const uint8_t* const* codes, const uint16_t* const* scales,
+                           const int64_t* N, int64_t K, const uint16_t* x, float* y,
+                           tq2_stream_t stream, bool silu_mul) {
+  tq2::MatSet m;
+  TQ2_TRY(build_matset(nmat, codes, scales, N, K, TQ2_MAX_K, &m));
+  if (!x || !y) return TQ2_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(y, 4)) return TQ2_ERR_ALIGN;
+  const size_t yb = (size_t)(silu_mul ? N[0] : m.rows) * 4;
+  if (!output_clear(y, yb, m, K, x, (size_t)K * 2)) return TQ2_ERR_ARG;
   (void)hipGetLastError();
+  if (silu_mul) return hip_status(tq2::launch_gemv_silu_mul(m, K, x, y, (hipStream_t)stream));
   return hip_status(tq2::launch_gemv_f16(m, K, x, y, (hipStream_t)stream));
 }
 
@@ -140,7 +164,7 @@ int32_t tq2_gemv(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_
                  const uint16_t* x, float* y, void* ws, size_t ws_bytes, tq2_stream_t stream) {
   (void)ws;
   (void)ws_bytes;
-  return gemv_common(&codes, &scales, 1, N, K, x, y, stream);
+  return gemv_common(1, &codes, &scales, &N, K, x, y, stream, false);
 }
 
 int32_t tq2_gemv_gate_up(const uint8_t* codes_g, const uint16_t* scales_g, const uint8_t* codes_u,
@@ -150,7 +174,28 @@ int32_t tq2_gemv_gate_up(const uint8_t* codes_g, const uint16_t* scales_g, const
   (void)ws_bytes;
   const uint8_t* c[2] = {codes_g, codes_u};
   const uint16_t* s[2] = {scales_g, scales_u};
-  return gemv_common(c, s, 2, N, K, x, y, stream);
+  const int64_t n[2] = {N, N};
+  return gemv_common(2, c, s, n, K, x, y, stream, false);
+}
+
+int32_t tq2_gemv_fused(int32_t nmat, const uint8_t* const* codes, const uint16_t* const* scales,
+                       const int64_t* N, int64_t K, const uint16_t* x, float* y, void* ws,
+                       size_t ws_bytes, tq2_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return gemv_common(nmat, codes, scales, N, K, x, y, stream, false);
+}
+
+int32_t tq2_gemv_gate_up_silu(const uint8_t* codes_g, const uint16_t* scales_g,
+                              const uint8_t* codes_u, const uint16_t* scales_u, int64_t N,
+                              int64_t K, const uint16_t* x, float* h, void* ws, size_t ws_bytes,
+                              tq2_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const uint8_t* c[2] = {codes_g, codes_u};
+  const uint16_t* s[2] = {scales_g, scales_u};
+  const int64_t n[2] = {N, N};
+  return gemv_common(2, c, s, n, K, x, h, stream, true);
 }
 
 int32_t tq2_quantize_i8(const uint16_t* x, int64_t K, float s, int8_t* x_q, tq2_stream_t stream) {
@@ -163,33 +208,36 @@ int32_t tq2_quantize_i8(const uint16_t* x, int64_t K, float s, int8_t* x_q, tq2_
   return hip_status(tq2::launch_quantize_i8(x, K, s, x_q, (hipStream_t)stream));
 }
 
-static int32_t i8_common(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
-                         const uint16_t* x, const int8_t* x_q, float s, float* y,
-                         int32_t* partials, tq2_stream_t stream) {
-  TQ2_TRY(check_shape(N, K, TQ2_I8_MAX_K));
-  if ((!x && !x_q) || !y) return TQ2_ERR_ARG;
-  TQ2_TRY(check_weights(codes, scales));
-  if ((x && !aligned(x, 16)) || (x_q && !aligned(x_q, 16)) || !aligned(y, 4) ||
-      (partials && !aligned(partials, 4)))
+// int8 matvec over nmat matrices; activations are fp16 x (quantized with s
+// in the kernel) or pre-quantized x_q; optional block partials (nmat == 1)
+// or output requantization with s_out.
+static int32_t i8_common(int nmat, const uint8_t* const* codes, const uint16_t* const* scales,
+                         const int64_t* N, int64_t K, const uint16_t* x, const int8_t* x_q,
+                         float s, float* y, int32_t* partials, const float* s_out,
+                         int8_t* y_q, float* y_deq, tq2_stream_t stream) {
+  tq2::MatSet m;
+  TQ2_TRY(build_matset(nmat, codes, scales, N, K, TQ2_I8_MAX_K, &m));
+  if (!x && !x_q) return TQ2_ERR_ARG;
+  if (s_out ? !y_q : !y) return TQ2_ERR_ARG;
+  if ((x && !aligned(x, 16)) || (x_q && !aligned(x_q, 16)) || (y && !aligned(y, 4)) ||
+      (partials && !aligned(partials, 4)) || (y_deq && !aligned(y_deq, 4)))
     return TQ2_ERR_ALIGN;
   TQ2_TRY(check_scale(s));
-  const size_t yb = (size_t)N * 4, pb = partials ? (size_t)(N * (K / 256)) * 4 : 0;
-  const size_t cb = (size_t)(N * K / 4), sb = (size_t)(N * K / 128);
+  if (s_out) TQ2_TRY(check_scale(*s_out));
   const void* in_ptr = x ? (const void*)x : (const void*)x_q;
   const size_t in_b = x ? (size_t)K * 2 : (size_t)K;
-  const void* outs[2] = {y, partials};
-  const size_t outb[2] = {yb, pb};
-  for (int i = 0; i < 2; ++i)
-    if (overlaps(outs[i], outb[i], codes, cb) || overlaps(outs[i], outb[i], scales, sb) ||
-        overlaps(outs[i], outb[i], in_ptr, in_b))
-      return TQ2_ERR_ARG;
-  if (overlaps(y, yb, partials, pb)) return TQ2_ERR_ARG;
-  tq2::MatSet m = {};
-  m.codes[0] = codes;
-  m.scales[0] = scales;
-  m.nmat = 1;
-  m.rows = (int32_t)N;
+  const size_t rows = (size_t)m.rows;
+  const void* outs[4] = {y, partials, y_q, y_deq};
+  const size_t outb[4] = {y ? rows * 4 : 0, partials ? (size_t)(m.rows * (K / 256)) * 4 : 0,
+                          y_q ? rows : 0, y_deq ? rows * 4 : 0};
+  for (int i = 0; i < 4; ++i) {
+    if (!output_clear(outs[i], outb[i], m, K, in_ptr, in_b)) return TQ2_ERR_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outb[i], outs[j], outb[j])) return TQ2_ERR_ARG;
+  }
   (void)hipGetLastError();
+  if (s_out)
+    return hip_status(tq2::launch_gemv_i8_requant(m, K, x, s, *s_out, y_q, y_deq, (hipStream_t)stream));
   return hip_status(tq2::launch_gemv_i8(m, K, x, x_q, s, y, partials, (hipStream_t)stream));
 }
 
@@ -199,7 +247,8 @@ int32_t tq2_gemv_i8q(const uint8_t* codes, const uint16_t* scales, int64_t N, in
   (void)ws;
   (void)ws_bytes;
   if (!x_q) return TQ2_ERR_ARG;
-  return i8_common(codes, scales, N, K, nullptr, x_q, s, y, partials, stream);
+  return i8_common(1, &codes, &scales, &N, K, nullptr, x_q, s, y, partials, nullptr, nullptr,
+                   nullptr, stream);
 }
 
 int32_t tq2_gemv_i8(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
@@ -208,7 +257,28 @@ int32_t tq2_gemv_i8(const uint8_t* codes, const uint16_t* scales, int64_t N, int
   (void)ws;
   (void)ws_bytes;
   if (!x) return TQ2_ERR_ARG;
-  return i8_common(codes, scales, N, K, x, nullptr, s, y, nullptr, stream);
+  return i8_common(1, &codes, &scales, &N, K, x, nullptr, s, y, nullptr, nullptr, nullptr,
+                   nullptr, stream);
+}
+
+int32_t tq2_gemv_i8_fused(int32_t nmat, const uint8_t* const* codes, const uint16_t* const* scales,
+                          const int64_t* N, int64_t K, const uint16_t* x, float s, float* y,
+                          void* ws, size_t ws_bytes, tq2_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!x) return TQ2_ERR_ARG;
+  return i8_common(nmat, codes, scales, N, K, x, nullptr, s, y, nullptr, nullptr, nullptr, nullptr,
+                   stream);
+}
+
+int32_t tq2_gemv_i8_requant(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                            const uint16_t* x, float s_in, float s_out, int8_t* y_q, float* y_deq,
+                            void* ws, size_t ws_bytes, tq2_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!x) return TQ2_ERR_ARG;
+  return i8_common(1, &codes, &scales, &N, K, x, nullptr, s_in, nullptr, nullptr, &s_out, y_q,
+                   y_deq, stream);
 }
 
 }  // extern "C"

@@ -33,10 +33,19 @@ hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x,
                            float* y, hipStream_t s);
 hipError_t launch_quantize_i8(const uint16_t* x, int64_t K, float scale,
                               int8_t* xq, hipStream_t s);
+// fp16 matvec over two matrices of m.row_begin[1] rows each (gate, up),
+// writing h[n] = silu(gate_n) * up_n only.
+hipError_t launch_gemv_silu_mul(const MatSet& m, int64_t K, const uint16_t* x,
+                                float* h, hipStream_t s);
 // int8 matvec; the activations come either as fp16 x (quantized inside the
 // kernel with scale s) or pre-quantized as xq (exactly one is non-null).
 hipError_t launch_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x,
                           const int8_t* xq, float s, float* y, int32_t* partials,
                           hipStream_t st);
+// int8 matvec from fp16 x, output requantized with s_out: y_q (int8) and,
+// if y_deq is non-null, y_q * s_out (fp32).
+hipError_t launch_gemv_i8_requant(const MatSet& m, int64_t K, const uint16_t* x,
+                                  float s, float s_out, int8_t* y_q, float* y_deq,
+                                  hipStream_t st);
 
 }  // namespace tq2

@@ -319,7 +319,34 @@ constexpr int kNonTemporal = 2;  // cache policy: streaming, read once
 // past K read k = 0) so that nothing waits on a branch; such rows and lanes
 // are zeroed later.  Each load is a raw buffer load: scalar descriptor for
 // the row, 32-bit lane offset, so there is no per-row vector address work.
-template <int R>
+//
+// Row spaces.  Plain: the wave's rows row0..row0+R-1 index the concatenation
+// of the MatSet's matrices.  PAIR (two matrices of N rows, gate and up): row
+// group g = row0/R takes gate rows g*R/2 .. g*R/2+R/2-1 as its first R/2
+// rows and the up rows with the same indices as its last R/2, so a wave ends
+// up holding both factors of each output of a fused SiLU(gate)*up.
+template <int R, bool PAIR>
+__device__ __forceinline__ bool row_valid(const MatSet& ms, int row0, int r) {
+  if constexpr (PAIR) return (row0 / R) * (R / 2) + (r % (R / 2)) < ms.row_begin[1];
+  else return row0 + r < ms.rows;
+}
+
+template <int R, bool PAIR>
+__device__ __forceinline__ RowPtr mapped_row(const MatSet& ms, int row0, int r, int64_t row_bytes,
+                                             int64_t BK) {
+  if constexpr (PAIR) {
+    const int np = ms.row_begin[1];
+    int n = (row0 / R) * (R / 2) + (r % (R / 2));
+    n = n < np ? n : np - 1;
+    const int m = r / (R / 2);
+    return RowPtr{ms.codes[m] + (int64_t)n * row_bytes, ms.scales[m] + (int64_t)n * BK};
+  } else {
+    const int row = row0 + r < ms.rows ? row0 + r : ms.rows - 1;
+    return row_ptr(ms, row, row_bytes, BK);
+  }
+}
+
+template <int R, bool PAIR = false>
 __device__ __forceinline__ void load_rows(const MatSet& ms, int row0, int64_t kk,
                                           int64_t row_bytes, int64_t BK, uint4 (&w)[R],
                                           uint16_t (&hs)[R]) {
@@ -327,8 +354,7 @@ __device__ __forceinline__ void load_rows(const MatSet& ms, int row0, int64_t kk
   const uint32_t soff = (uint32_t)(kk / kBlock) * 2u;      // byte offset in a scale row
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int row = row0 + r < ms.rows ? row0 + r : ms.rows - 1;
-    const RowPtr rp = row_ptr(ms, row, row_bytes, BK);
+    const RowPtr rp = mapped_row<R, PAIR>(ms, row0, r, row_bytes, BK);
     const v4u t = __builtin_bit_cast(
         v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc(rp.codes, (uint32_t)row_bytes), (int)coff, 0,
                                                    kNonTemporal));
@@ -349,9 +375,15 @@ __host__ __device__ inline size_t f16_lds_bytes(int C, int S, int R) {
   return (size_t)C * 8 * 64 * 16 + (size_t)C * 64 * 16 + (size_t)C * S * R * 4;
 }
 
+enum Epilogue { kStoreF32 = 0, kSiluMul = 1, kRequant = 2 };
+
+// h = silu(g) * u with silu(v) = v / (1 + exp(-v)), fp32
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 // CT: chunk-waves per row group as a compile-time constant (1, 2, 4), or 0
-// to take it from `sp` at run time.
-template <int R, int CT, int MAXT>
+// to take it from `sp` at run time.  EPI: kStoreF32 writes y per row;
+// kSiluMul runs over PAIR rows and writes silu(gate)*up per output.
+template <int R, int CT, int MAXT, int EPI = kStoreF32>
 __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
                                                    const uint16_t* __restrict__ x,
                                                    float* __restrict__ y, Split sp) {
@@ -381,9 +413,10 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   const int g0 = tid < ngroups ? tid : ngroups - 1;
   const uint4 xa = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)g0);
   const uint4 xb = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)g0 + 8);
+  constexpr bool PAIR = EPI == kSiluMul;
   uint4 w[R];
   uint16_t hs[R];
-  load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs);
+  load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs);
   __builtin_amdgcn_sched_barrier(0);
 
   // (2) stage: group m covers weights 16m..16m+15 = group (m % 4) of lane
@@ -440,7 +473,7 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint32_t keep = row0 + r < ms.rows ? 0xFFFFu : 0u;
+    const uint32_t keep = row_valid<R, PAIR>(ms, row0, r) ? 0xFFFFu : 0u;
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hs[r] & keep));
     acc[r] = __builtin_fmaf((float)d, lane_dot_f16(w[r], xp, seed), 0.0f);  // v_fma_mix
   }
@@ -448,11 +481,25 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   reduce_rows_f32<R>(acc, out);
   const int rho = lane >> 4;
   if (C == 1) {
-    if ((lane & 15) == 0) {
+    if constexpr (EPI == kSiluMul) {
+      // rows of the first half (gate) sit in lanes 0..31, their up partners
+      // (row + R/2) at lane + 32
 #pragma unroll
       for (int i = 0; i < kOut<R>; ++i) {
+        float a = out[i], b = out[i];
+        swap32(a, b);  // b: lanes 0..31 now hold lanes 32..63
         const int rr = reduced_row<R>(i, rho);
-        if (rr >= 0 && row0 + rr < ms.rows) y[row0 + rr] = ldexpf(out[i], 18);
+        const int n = (row0 / R) * (R / 2) + rr;
+        if ((lane & 15) == 0 && lane < 32 && rr >= 0 && n < ms.row_begin[1])
+          y[n] = silu_mul(ldexpf(out[i], 18), ldexpf(b, 18));
+      }
+    } else {
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < kOut<R>; ++i) {
+          const int rr = reduced_row<R>(i, rho);
+          if (rr >= 0 && row0 + rr < ms.rows) y[row0 + rr] = ldexpf(out[i], 18);
+        }
       }
     }
     return;
@@ -466,10 +513,22 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
     }
   }
   __syncthreads();
-  if (c == 0 && lane < R) {
-    float tsum = red[wave * R + lane];
-    for (int cc = 1; cc < C; ++cc) tsum += red[(wave + cc) * R + lane];
-    if (row0 + lane < ms.rows) y[row0 + lane] = ldexpf(tsum, 18);
+  if constexpr (EPI == kSiluMul) {
+    if (c == 0 && lane < R / 2) {
+      float g = red[wave * R + lane], u = red[wave * R + lane + R / 2];
+      for (int cc = 1; cc < C; ++cc) {
+        g += red[(wave + cc) * R + lane];
+        u += red[(wave + cc) * R + lane + R / 2];
+      }
+      const int n = (row0 / R) * (R / 2) + lane;
+      if (n < ms.row_begin[1]) y[n] = silu_mul(ldexpf(g, 18), ldexpf(u, 18));
+    }
+  } else {
+    if (c == 0 && lane < R) {
+      float tsum = red[wave * R + lane];
+      for (int cc = 1; cc < C; ++cc) tsum += red[(wave + cc) * R + lane];
+      if (row0 + lane < ms.rows) y[row0 + lane] = ldexpf(tsum, 18);
+    }
   }
 }
 
@@ -506,28 +565,29 @@ static hipError_t set_lds_cap(const void* fn) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
-template <int R>
+template <int R, int EPI>
 static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
                                hipStream_t s) {
   const Split sp = pick_split(K);
-  const int64_t groups = (m.rows + R - 1) / R;
+  // PAIR rows: R/2 outputs per row group, each reading one gate and one up row
+  const int64_t groups = EPI == kSiluMul ? (m.row_begin[1] + R / 2 - 1) / (R / 2) : (m.rows + R - 1) / R;
   const dim3 grid((unsigned)((groups + sp.S - 1) / sp.S));
   const size_t lds = f16_lds_bytes(sp.C, sp.S, R);
   const dim3 block(64 * sp.C * sp.S);
   if (sp.C == 1) {
-    hipLaunchKernelGGL((k_gemv_f16<R, 1, 512>), grid, block, lds, s, m, K, x, y, sp);
+    hipLaunchKernelGGL((k_gemv_f16<R, 1, 512, EPI>), grid, block, lds, s, m, K, x, y, sp);
   } else if (sp.C == 2) {
-    hipLaunchKernelGGL((k_gemv_f16<R, 2, 512>), grid, block, lds, s, m, K, x, y, sp);
+    hipLaunchKernelGGL((k_gemv_f16<R, 2, 512, EPI>), grid, block, lds, s, m, K, x, y, sp);
   } else if (sp.C == 4) {
-    hipLaunchKernelGGL((k_gemv_f16<R, 4, 1024>), grid, block, lds, s, m, K, x, y, sp);
+    hipLaunchKernelGGL((k_gemv_f16<R, 4, 1024, EPI>), grid, block, lds, s, m, K, x, y, sp);
   } else if (block.x <= 512) {
-    hipLaunchKernelGGL((k_gemv_f16<R, 0, 512>), grid, block, lds, s, m, K, x, y, sp);
+    hipLaunchKernelGGL((k_gemv_f16<R, 0, 512, EPI>), grid, block, lds, s, m, K, x, y, sp);
   } else {
     if (lds > 64 * 1024) {
-      const hipError_t e = set_lds_cap(reinterpret_cast<const void*>(&k_gemv_f16<R, 0, 1024>));
+      const hipError_t e = set_lds_cap(reinterpret_cast<const void*>(&k_gemv_f16<R, 0, 1024, EPI>));
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_gemv_f16<R, 0, 1024>), grid, block, lds, s, m, K, x, y, sp);
+    hipLaunchKernelGGL((k_gemv_f16<R, 0, 1024, EPI>), grid, block, lds, s, m, K, x, y, sp);
   }
   return hipGetLastError();
 }
@@ -535,9 +595,18 @@ static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, fl
 hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
                            hipStream_t s) {
   switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 16, 8)) {
-    case 8: return run_gemv_f16<8>(m, K, x, y, s);
-    case 4: return run_gemv_f16<4>(m, K, x, y, s);
-    default: return run_gemv_f16<2>(m, K, x, y, s);
+    case 8: return run_gemv_f16<8, kStoreF32>(m, K, x, y, s);
+    case 4: return run_gemv_f16<4, kStoreF32>(m, K, x, y, s);
+    default: return run_gemv_f16<2, kStoreF32>(m, K, x, y, s);
+  }
+}
+
+hipError_t launch_gemv_silu_mul(const MatSet& m, int64_t K, const uint16_t* x, float* h,
+                                hipStream_t s) {
+  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 16, 8)) {
+    case 8: return run_gemv_f16<8, kSiluMul>(m, K, x, h, s);
+    case 4: return run_gemv_f16<4, kSiluMul>(m, K, x, h, s);
+    default: return run_gemv_f16<2, kSiluMul>(m, K, x, h, s);
   }
 }
 
@@ -686,12 +755,35 @@ __host__ __device__ inline size_t i8_lds_bytes(int C, int S, int R) {
 // pre-quantized, and stages them in LDS in the dword order of lane_dot_i8.
 // Partials are exact and so is the cross-wave sum: the output does not depend
 // on the reduction order at all.
-template <int R, bool QUANT, bool PARTIALS, int CT, int MAXT>
+// Output requantization (page "gemma4 wNa8o8 requires int8 activations",
+// recipe paragraph): y_q = clamp(rint(y / s_out), -128, 127) from the exact
+// fp32 y, one IEEE division; y_deq = y_q * s_out (fp32), when requested.
+struct Requant {
+  float s_out;
+  int8_t* y_q;
+  float* y_deq;  // nullable
+};
+
+__device__ __forceinline__ void store_i8(float* y, const Requant& rq, int64_t row, float v,
+                                         bool requant) {
+  if (!requant) {
+    y[row] = v;
+    return;
+  }
+  float r = __builtin_rintf(v / rq.s_out);
+  if (__builtin_isnan(r)) r = 0.0f;
+  r = fminf(fmaxf(r, -128.0f), 127.0f);
+  rq.y_q[row] = (int8_t)(int)r;
+  if (rq.y_deq) rq.y_deq[row] = r * rq.s_out;
+}
+
+template <int R, bool QUANT, bool PARTIALS, int CT, int MAXT, bool REQUANT = false>
 __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
                                                   const uint16_t* __restrict__ x,
                                                   const int8_t* __restrict__ xq_in, float s,
                                                   float* __restrict__ y,
-                                                  int32_t* __restrict__ partials, Split sp) {
+                                                  int32_t* __restrict__ partials, Split sp,
+                                                  Requant rq) {
   extern __shared__ uint4 lds[];
   const int C = CT ? CT : sp.C, S = sp.S;
   uint4* xs = lds;                                            // [C][4][64]
@@ -795,7 +887,7 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
 #pragma unroll
       for (int i = 0; i < kOut<R>; ++i) {
         const int rr = reduced_row<R>(i, rho);
-        if (rr >= 0 && row0 + rr < ms.rows) y[row0 + rr] = i8_epilogue(out[i], s);
+        if (rr >= 0 && row0 + rr < ms.rows) store_i8(y, rq, row0 + rr, i8_epilogue(out[i], s), REQUANT);
       }
     }
     return;
@@ -811,50 +903,64 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
   if (c == 0 && lane < R) {
     int64_t tsum = red[wave * R + lane];
     for (int cc = 1; cc < C; ++cc) tsum += red[(wave + cc) * R + lane];
-    if (row0 + lane < ms.rows) y[row0 + lane] = i8_epilogue(tsum, s);
+    if (row0 + lane < ms.rows) store_i8(y, rq, row0 + lane, i8_epilogue(tsum, s), REQUANT);
   }
 }
 
-template <int R, bool QUANT, bool PARTIALS>
+template <int R, bool QUANT, bool PARTIALS, bool REQUANT>
 static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
-                              float s, float* y, int32_t* partials, hipStream_t st) {
+                              float s, float* y, int32_t* partials, const Requant& rq,
+                              hipStream_t st) {
   const Split sp = pick_split(K);
   const int64_t groups = (m.rows + R - 1) / R;
   const int64_t grid = (groups + sp.S - 1) / sp.S;
   const size_t lds = i8_lds_bytes(sp.C, sp.S, R);
-  const int threads = 64 * sp.C * sp.S;
+  const dim3 g((unsigned)grid), b(64 * sp.C * sp.S);
   if (sp.C == 1)
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 1, 512>), dim3((unsigned)grid), dim3(threads), lds,
-                       st, m, K, x, xq, s, y, partials, sp);
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 1, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, y,
+                       partials, sp, rq);
   else if (sp.C == 4)
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 4, 1024>), dim3((unsigned)grid), dim3(threads), lds,
-                       st, m, K, x, xq, s, y, partials, sp);
-  else if (threads <= 512)
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 512>), dim3((unsigned)grid), dim3(threads), lds,
-                       st, m, K, x, xq, s, y, partials, sp);
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 4, 1024, REQUANT>), g, b, lds, st, m, K, x, xq, s,
+                       y, partials, sp, rq);
+  else if (b.x <= 512)
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, y,
+                       partials, sp, rq);
   else
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 1024>), dim3((unsigned)grid), dim3(threads), lds,
-                       st, m, K, x, xq, s, y, partials, sp);
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 1024, REQUANT>), g, b, lds, st, m, K, x, xq, s,
+                       y, partials, sp, rq);
   return hipGetLastError();
 }
 
 template <int R>
 static hipError_t run_gemv_i8_r(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
-                                float s, float* y, int32_t* partials, hipStream_t st) {
+                                float s, float* y, int32_t* partials, const Requant* rq,
+                                hipStream_t st) {
+  const Requant none = {1.0f, nullptr, nullptr};
+  if (rq) return run_gemv_i8<R, true, false, true>(m, K, x, xq, s, y, partials, *rq, st);
   if (x) {
-    if (partials) return run_gemv_i8<R, true, true>(m, K, x, xq, s, y, partials, st);
-    return run_gemv_i8<R, true, false>(m, K, x, xq, s, y, partials, st);
+    if (partials) return run_gemv_i8<R, true, true, false>(m, K, x, xq, s, y, partials, none, st);
+    return run_gemv_i8<R, true, false, false>(m, K, x, xq, s, y, partials, none, st);
   }
-  if (partials) return run_gemv_i8<R, false, true>(m, K, x, xq, s, y, partials, st);
-  return run_gemv_i8<R, false, false>(m, K, x, xq, s, y, partials, st);
+  if (partials) return run_gemv_i8<R, false, true, false>(m, K, x, xq, s, y, partials, none, st);
+  return run_gemv_i8<R, false, false, false>(m, K, x, xq, s, y, partials, none, st);
 }
 
 hipError_t launch_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
                           float s, float* y, int32_t* partials, hipStream_t st) {
   switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 16, 8)) {
-    case 8: return run_gemv_i8_r<8>(m, K, x, xq, s, y, partials, st);
-    case 4: return run_gemv_i8_r<4>(m, K, x, xq, s, y, partials, st);
-    default: return run_gemv_i8_r<2>(m, K, x, xq, s, y, partials, st);
+    case 8: return run_gemv_i8_r<8>(m, K, x, xq, s, y, partials, nullptr, st);
+    case 4: return run_gemv_i8_r<4>(m, K, x, xq, s, y, partials, nullptr, st);
+    default: return run_gemv_i8_r<2>(m, K, x, xq, s, y, partials, nullptr, st);
+  }
+}
+
+hipError_t launch_gemv_i8_requant(const MatSet& m, int64_t K, const uint16_t* x, float s,
+                                  float s_out, int8_t* y_q, float* y_deq, hipStream_t st) {
+  const Requant rq = {s_out, y_q, y_deq};
+  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 16, 8)) {
+    case 8: return run_gemv_i8_r<8>(m, K, x, nullptr, s, nullptr, nullptr, &rq, st);
+    case 4: return run_gemv_i8_r<4>(m, K, x, nullptr, s, nullptr, nullptr, &rq, st);
+    default: return run_gemv_i8_r<2>(m, K, x, nullptr, s, nullptr, nullptr, &rq, st);
   }
 }
 

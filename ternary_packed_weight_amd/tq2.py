@@ -51,12 +51,21 @@ _lib.tq2_gemv_i8q.argtypes = [_P, _P, _I64, _I64, _P, _F, _P, _P, _P, _SZ, _P]
 _lib.tq2_gemv_i8q.restype = _I32
 _lib.tq2_gemv_i8.argtypes = [_P, _P, _I64, _I64, _P, _F, _P, _P, _SZ, _P]
 _lib.tq2_gemv_i8.restype = _I32
+_lib.tq2_gemv_fused.argtypes = [_I32, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
+_lib.tq2_gemv_fused.restype = _I32
+_lib.tq2_gemv_i8_fused.argtypes = [_I32, _P, _P, _P, _I64, _P, _F, _P, _P, _SZ, _P]
+_lib.tq2_gemv_i8_fused.restype = _I32
+_lib.tq2_gemv_gate_up_silu.argtypes = [_P, _P, _P, _P, _I64, _I64, _P, _P, _P, _SZ, _P]
+_lib.tq2_gemv_gate_up_silu.restype = _I32
+_lib.tq2_gemv_i8_requant.argtypes = [_P, _P, _I64, _I64, _P, _F, _F, _P, _P, _P, _SZ, _P]
+_lib.tq2_gemv_i8_requant.restype = _I32
 
 TQ2_OK = 0
 TQ2_OP_GEMV, TQ2_OP_GATE_UP, TQ2_OP_GEMV_I8, TQ2_OP_GEMV_I8Q = 0, 1, 2, 3
 EXPORTED = ("tq2_abi_version", "tq2_status_string", "tq2_codes_bytes", "tq2_scales_bytes",
             "tq2_workspace_bytes", "tq2_pack", "tq2_dequant", "tq2_gemv", "tq2_gemv_gate_up",
-            "tq2_quantize_i8", "tq2_gemv_i8q", "tq2_gemv_i8")
+            "tq2_quantize_i8", "tq2_gemv_i8q", "tq2_gemv_i8", "tq2_gemv_fused", "tq2_gemv_i8_fused",
+            "tq2_gemv_gate_up_silu", "tq2_gemv_i8_requant")
 
 
 class Tq2Error(RuntimeError):
@@ -205,3 +214,71 @@ def tq2_gemv_i8(codes, scales, x, s, y=None, ws=None, stream=None):
     _check("tq2_gemv_i8", _lib.tq2_gemv_i8(_ptr(codes), _ptr(scales), N, K, _ptr(x), float(s),
                                            _ptr(y), _ptr(ws), wsb, _stream(stream)))
     return y
+
+
+def _host_arrays(mats):
+    """Host pointer/size arrays for the fused entry points: mats is a list
+    of (codes, scales) device tensors sharing K."""
+    if not 1 <= len(mats) <= 3:
+        raise ValueError("1 to 3 matrices")
+    shapes = [_shape(c, s) for c, s in mats]
+    K = shapes[0][1]
+    if any(k != K for _, k in shapes):
+        raise ValueError("fused matrices must share K")
+    n = len(mats)
+    cp = (ctypes.c_void_p * n)(*[c.data_ptr() for c, _ in mats])
+    sp = (ctypes.c_void_p * n)(*[s.data_ptr() for _, s in mats])
+    Np = (ctypes.c_int64 * n)(*[N for N, _ in shapes])
+    return n, cp, sp, Np, [N for N, _ in shapes], K
+
+
+def tq2_gemv_fused(mats, x, y=None, ws=None, stream=None):
+    """y = concatenation of W_i x over mats = [(codes_i, scales_i), ...]."""
+    n, cp, sp, Np, Ns, K = _host_arrays(mats)
+    _dev(x, "x")
+    if y is None:
+        y = torch.empty(sum(Ns), dtype=torch.float32, device=x.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("tq2_gemv_fused", _lib.tq2_gemv_fused(n, cp, sp, Np, K, _ptr(x), _ptr(y), _ptr(ws), wsb,
+                                                 _stream(stream)))
+    return y
+
+
+def tq2_gemv_i8_fused(mats, x, s, y=None, ws=None, stream=None):
+    n, cp, sp, Np, Ns, K = _host_arrays(mats)
+    _dev(x, "x")
+    if y is None:
+        y = torch.empty(sum(Ns), dtype=torch.float32, device=x.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("tq2_gemv_i8_fused", _lib.tq2_gemv_i8_fused(n, cp, sp, Np, K, _ptr(x), float(s), _ptr(y),
+                                                       _ptr(ws), wsb, _stream(stream)))
+    return y
+
+
+def tq2_gemv_gate_up_silu(codes_g, scales_g, codes_u, scales_u, x, h=None, ws=None, stream=None):
+    N, K = _shape(codes_g, scales_g)
+    if _shape(codes_u, scales_u) != (N, K):
+        raise ValueError("gate and up must have the same shape")
+    _dev(x, "x")
+    if h is None:
+        h = torch.empty(N, dtype=torch.float32, device=codes_g.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("tq2_gemv_gate_up_silu", _lib.tq2_gemv_gate_up_silu(
+        _ptr(codes_g), _ptr(scales_g), _ptr(codes_u), _ptr(scales_u), N, K, _ptr(x), _ptr(h),
+        _ptr(ws), wsb, _stream(stream)))
+    return h
+
+
+def tq2_gemv_i8_requant(codes, scales, x, s_in, s_out, y_q=None, y_deq=None, want_deq=True,
+                        ws=None, stream=None):
+    N, K = _shape(codes, scales)
+    _dev(x, "x")
+    if y_q is None:
+        y_q = torch.empty(N, dtype=torch.int8, device=codes.device)
+    if y_deq is None and want_deq:
+        y_deq = torch.empty(N, dtype=torch.float32, device=codes.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("tq2_gemv_i8_requant", _lib.tq2_gemv_i8_requant(
+        _ptr(codes), _ptr(scales), N, K, _ptr(x), float(s_in), float(s_out), _ptr(y_q), _ptr(y_deq),
+        _ptr(ws), wsb, _stream(stream)))
+    return y_q, y_deq

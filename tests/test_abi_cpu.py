@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("tq2_pack", "tq2_gemv", "tq2_gemv_gate_up", "tq2_gemv_i8", "tq2_gemv_i8q",
-                     "tq2_quantize_i8", "tq2_dequant", "tq2_workspace_bytes"):
+                     "tq2_quantize_i8", "tq2_dequant", "tq2_workspace_bytes", "tq2_gemv_fused",
+                     "tq2_gemv_i8_fused", "tq2_gemv_gate_up_silu", "tq2_gemv_i8_requant"):
         assert required in names
 
 
@@ -130,3 +131,32 @@ def test_error_paths_pack(tq2):
     assert lib.tq2_pack(P(0), 4, 256, P(C), P(S), P(B), None) == 1
     assert lib.tq2_dequant(P(C), P(S), 4, 256, P(0), None) == 1
     assert lib.tq2_dequant(P(C), P(S), 4, 256, P(C), None) == 1
+
+
+@no_gpu
+def test_error_paths_fused_and_epilogues(tq2):
+    lib = tq2.lib()
+    C = (ctypes.c_void_p * 3)(A, A + 2 ** 20, A + 2 ** 21)
+    S = (ctypes.c_void_p * 3)(A + 2 ** 22, A + 2 ** 22 + 2 ** 16, A + 2 ** 22 + 2 ** 17)
+    N = (ctypes.c_int64 * 3)(4096, 256, 256)
+    x, y = A + 2 ** 25, A + 2 ** 26
+
+    def f(nmat=3, n=N, K=4096, xx=x, yy=y):
+        return lib.tq2_gemv_fused(nmat, C, S, n, K, P(xx), P(yy), None, 0, None)
+
+    assert f(nmat=0) == 1 and f(nmat=4) == 1
+    assert f(n=(ctypes.c_int64 * 3)(4096, 0, 256)) == 1
+    assert f(n=(ctypes.c_int64 * 3)(2 ** 29, 2 ** 29, 2 ** 29), K=256) == 2   # rows >= 2^31
+    assert f(K=1000) == 2 and f(xx=x + 4) == 3 and f(yy=A + 2 ** 20 + 16) == 1
+    assert lib.tq2_gemv_fused(2, None, S, N, 4096, P(x), P(y), None, 0, None) == 1
+    assert lib.tq2_gemv_i8_fused(3, C, S, N, 4096, P(x), ctypes.c_float(0.0), P(y), None, 0, None) == 5
+    assert lib.tq2_gemv_i8_fused(3, C, S, N, 65536, P(x), ctypes.c_float(1.0), P(y), None, 0, None) == 2
+    assert lib.tq2_gemv_gate_up_silu(P(A), P(A + 4096), P(A + 2 ** 20), P(A + 2 ** 20 + 4096), 16, 256,
+                                     P(x), P(0), None, 0, None) == 1
+    assert lib.tq2_gemv_gate_up_silu(P(A), P(A + 4096), P(A + 2 ** 20), P(A + 2 ** 20 + 4096), 16, 256,
+                                     P(x), P(A + 64), None, 0, None) == 1
+    rq = lambda s_in=0.1, s_out=0.1, yq=y, yd=A + 2 ** 27: lib.tq2_gemv_i8_requant(
+        P(A), P(A + 2 ** 24), 16, 256, P(x), ctypes.c_float(s_in), ctypes.c_float(s_out), P(yq), P(yd),
+        None, 0, None)
+    assert rq(s_out=0.0) == 5 and rq(s_out=float("nan")) == 5 and rq(s_in=-1.0) == 5
+    assert rq(yq=0) == 1 and rq(yd=A + 2 ** 27 + 2) == 3 and rq(yd=y) == 1

@@ -338,3 +338,84 @@ def test_gemv_i8_determinism_and_negation(tq2):
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     assert torch.equal(yn, -y1)
+
+
+# ------------------------------------------------- fused linears, epilogues
+
+@pytest.mark.parametrize("Ns,K", [((4096, 256, 256), 4096), ((33, 7, 130), 768), ((5, 9), 16384)])
+def test_fused_fp16_matches_single_calls(tq2, Ns, K):
+    """q/k/v-style fusion: one kernel over up to three matrices sharing x.
+    Each output equals the single-matrix call bit for bit (same per-row
+    arithmetic) and is within tolerance of the oracle."""
+    mats, host = [], []
+    x = None
+    for i, N in enumerate(Ns):
+        _, c, s, xx = _packed(1300 + 7 * i + N, N, K)
+        x = xx if x is None else x
+        host.append((c, s))
+        mats.append(_to_dev(c, s))
+    xd = torch.from_numpy(x).to(DEV)
+    y = tq2.tq2_gemv_fused(mats, xd)
+    singles = [tq2.tq2_gemv(c, s, xd) for (c, s) in mats]
+    torch.cuda.synchronize()
+    off = 0
+    for (c, s), ys, N in zip(host, singles, Ns):
+        assert torch.equal(y[off:off + N], ys)
+        _check_f16(y[off:off + N].cpu().numpy(), oracle.gemv(c, s, N, K, synth.bits(x)), _tol(s, x, N, K))
+        off += N
+
+
+@pytest.mark.parametrize("Ns,K", [((4096, 256, 256), 4096), ((16384, 16384), 4096), ((3, 65), 16384)])
+def test_fused_int8_bit_exact(tq2, Ns, K):
+    mats, host = [], []
+    x = None
+    for i, N in enumerate(Ns):
+        _, c, s, xx = _packed(1400 + 7 * i + N, N, K)
+        x = xx if x is None else x
+        host.append((c, s))
+        mats.append(_to_dev(c, s))
+    sc = np.float32(np.float32(np.abs(x.astype(np.float32)).max()) / np.float32(100))
+    xd = torch.from_numpy(x).to(DEV)
+    y = tq2.tq2_gemv_i8_fused(mats, xd, sc)
+    torch.cuda.synchronize()
+    yc = y.cpu().numpy()
+    off = 0
+    for (c, s), N in zip(host, Ns):
+        ref = oracle.gemv_i8(c, s, N, K, synth.bits(x), sc)
+        assert np.array_equal(yc[off:off + N].view(np.uint32), ref.view(np.uint32))
+        off += N
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 768), (2048, 4096), (16384, 4096), (130, 16384)])
+def test_gate_up_silu(tq2, N, K):
+    """h = silu(g)*u against the oracle: g, u each within the fp16 tolerance
+    and the fp32 epilogue within a few ulp."""
+    _, cg, sg, x = _packed(1500 + N, N, K)
+    _, cu, su, _ = _packed(1600 + N, N, K)
+    dcg, dsg, xd = _to_dev(cg, sg, x)
+    dcu, dsu = _to_dev(cu, su)
+    h = tq2.tq2_gemv_gate_up_silu(dcg, dsg, dcu, dsu, xd)
+    torch.cuda.synchronize()
+    g = oracle.gemv(cg, sg, N, K, synth.bits(x)).astype(np.float64)
+    u = oracle.gemv(cu, su, N, K, synth.bits(x)).astype(np.float64)
+    tg, tu = _tol(sg, x, N, K), _tol(su, x, N, K)
+    href = oracle.silu_mul(g.astype(np.float32), u.astype(np.float32))
+    silu = g / (1 + np.exp(-g))
+    bound = 1.1 * tg * (np.abs(u) + tu) + (np.abs(silu) + 1.1 * tg) * tu + 1e-5 * np.abs(href) + 1e-6
+    err = np.abs(h.cpu().numpy().astype(np.float64) - href)
+    assert np.all(err <= bound), (np.argmax(err / bound), float((err / bound).max()))
+
+
+@pytest.mark.parametrize("N,K,div_in,s_out", [(4096, 16384, 100, 0.05), (33, 768, 200, 0.002), (5, 4352, 100, 0.5)])
+def test_int8_requant_bit_exact(tq2, N, K, div_in, s_out):
+    _, c, s, x = _packed(1700 + N, N, K, outliers=(div_in == 200))
+    s_in = np.float32(np.float32(np.abs(x.astype(np.float32)).max()) / np.float32(div_in))
+    dc, ds, xd = _to_dev(c, s, x)
+    yq, yd = tq2.tq2_gemv_i8_requant(dc, ds, xd, s_in, np.float32(s_out))
+    torch.cuda.synchronize()
+    y_ref = oracle.gemv_i8(c, s, N, K, synth.bits(x), s_in)
+    yq_ref, yd_ref = oracle.requant_i8(y_ref, np.float32(s_out))
+    assert np.array_equal(yq.cpu().numpy(), yq_ref)
+    assert np.array_equal(yd.cpu().numpy().view(np.uint32), yd_ref.view(np.uint32))
+    if s_out == 0.002:
+        assert np.count_nonzero(np.abs(yq_ref.astype(np.int32)) >= 127) > 0   # saturation exercised

@@ -350,3 +350,38 @@ def test_int8_large_scales_exact():
     xq = oracle.quantize_i8(synth.bits(x), s)
     y, _ = oracle.gemv_i8q(_fields_to_bytes(q), synth.bits(d), N, K, xq, s)
     assert np.array_equal(y, brute.exact_i8_y(q, synth.bits(d), xq, s))
+
+
+# ---------------------------------------------------------------- epilogues
+
+def test_requant_golden():
+    for line in _lines("requant_i8.txt"):
+        s, y, eq, ed = line.split()[:4]
+        yq, yd = oracle.requant_i8(np.array([float(y)], np.float32), np.float32(float(s)))
+        assert int(yq[0]) == int(eq) and float(yd[0]) == float(ed), line
+
+
+def test_requant_properties():
+    """Monotone, saturating, and y_deq = y_q * s_out exactly where the product
+    is representable."""
+    y = (synth.rng(1201).standard_normal(5000) * 3).astype(np.float32)
+    yq, yd = oracle.requant_i8(y, np.float32(0.02))
+    order = np.argsort(y, kind="stable")
+    assert np.all(np.diff(yq[order].astype(np.int32)) >= 0)
+    assert yq.min() == -128 and yq.max() == 127
+    assert np.array_equal(yd, (yq.astype(np.float32) * np.float32(0.02)).astype(np.float32))
+    inside = (yq > -128) & (yq < 127)
+    assert np.all(np.abs(yd[inside].astype(np.float64) - y[inside]) <= 0.01 * (1 + 1e-6))
+
+
+def test_silu_mul_reference():
+    """silu(v) = v / (1 + e^-v): closed forms and the math library."""
+    g = np.array([0.0, 1.0, -1.0, 30.0, -30.0, 0.5, -700.0], np.float32)
+    u = np.array([3.0, 2.0, 2.0, 1.0, 1.0, -4.0, 1.0], np.float32)
+    h = oracle.silu_mul(g, u)
+    ref = [float(a) / (1.0 + math.exp(-float(a))) * float(b) for a, b in zip(g, u)]
+    assert h[0] == 0.0
+    assert np.allclose(h, ref, rtol=1e-15, atol=0)
+    # silu(v) -> v as v -> inf and -> -v e^v as v -> -inf
+    assert abs(h[3] - 30.0) < 1e-11 and abs(h[4] + 30.0 * math.exp(-30.0)) < 1e-20
+    assert h[6] < 0 and abs(h[6]) < 1e-290
