@@ -369,10 +369,14 @@ struct Split {
   int S;  // row groups per workgroup
 };
 
+__host__ __device__ constexpr int f16_stage_passes(int CT) { return CT ? 1 : 4; }
+
+
 // LDS of the fp16 matvec: x pairs [C][8][64] uint4, group sums [C][64] float4,
+// a sink [3] uint4 for the stores of threads with no group to stage,
 // cross-wave row sums [C*S][R] float.
 __host__ __device__ inline size_t f16_lds_bytes(int C, int S, int R) {
-  return (size_t)C * 8 * 64 * 16 + (size_t)C * 64 * 16 + (size_t)C * S * R * 4;
+  return (size_t)C * 8 * 64 * 16 + (size_t)C * 64 * 16 + 3 * 16 + (size_t)C * S * R * 4;
 }
 
 enum Epilogue { kStoreF32 = 0, kSiluMul = 1, kRequant = 2 };
@@ -391,7 +395,8 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   const int C = CT ? CT : sp.C, S = sp.S;
   uint4* xpairs = lds;                                          // [C][8][64]
   float4* gsum = reinterpret_cast<float4*>(lds + C * 8 * 64);   // [C][64]
-  float* red = reinterpret_cast<float*>(gsum + C * 64);         // [C*S][R]
+  uint4* sink = reinterpret_cast<uint4*>(gsum + C * 64);        // [3]
+  float* red = reinterpret_cast<float*>(sink + 3);              // [C*S][R]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -407,12 +412,23 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   const int64_t BK = K / kBlock;
   const int ngroups = (int)(K / 16);  // 16-weight groups to stage
 
-  // (1) loads: one 16-weight group of x per thread (two 16-byte reads,
+  // (1) loads: XP 16-weight groups of x per thread (two 16-byte reads each,
   //     coalesced across the workgroup; clamped, so unconditional), then
-  //     this wave's weights.
-  const int g0 = tid < ngroups ? tid : ngroups - 1;
-  const uint4 xa = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)g0);
-  const uint4 xb = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)g0 + 8);
+  //     this wave's weights.  x goes first and stays first: the wait for it
+  //     counts loads in issue order, so weights issued before x would hold
+  //     the staging (and the barrier) until every weight had arrived.
+  // staging passes over the C*256 groups: the launcher guarantees
+  // XP * blockDim >= C*256 (one pass for C <= 4, four for the runtime-C form)
+  constexpr int XP = f16_stage_passes(CT);
+  uint4 xa[XP], xb[XP];
+#pragma unroll
+  for (int p = 0; p < XP; ++p) {
+    const int m = tid + p * (int)blockDim.x;
+    const int gm = m < ngroups ? m : ngroups - 1;
+    xa[p] = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm);
+    xb[p] = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm + 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   constexpr bool PAIR = EPI == kSiluMul;
   uint4 w[R];
   uint16_t hs[R];
@@ -424,13 +440,14 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   //     2(m%4) and 2(m%4)+1 of that lane; its x sum to gsum[..].(m % 4).
   //     Groups past K (a partial last chunk) are staged as zeros, so lanes
   //     beyond K contribute exactly 0.
-  for (int m = tid; m < C * 256; m += blockDim.x) {
-    uint4 a4 = xa, b4 = xb;
-    if (m != tid) {  // second pass (K > 8 * blockDim): rare
-      const int gm = m < ngroups ? m : ngroups - 1;
-      a4 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm);
-      b4 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm + 8);
-    }
+  //     Every thread runs the arithmetic and stores; one without a group
+  //     stores into the sink.  (A branch around it would let the compiler
+  //     sink the x loads behind the weight loads, into the branch.)
+#pragma unroll
+  for (int p = 0; p < XP; ++p) {
+    const int m = tid + p * (int)blockDim.x;
+    const bool staged = m < C * 256;
+    const uint4 a4 = xa[p], b4 = xb[p];
     const uint32_t z = m < ngroups ? 0xFFFFFFFFu : 0u;
     const uint32_t xw[8] = {a4.x & z, a4.y & z, a4.z & z, a4.w & z,
                             b4.x & z, b4.y & z, b4.z & z, b4.w & z};
@@ -452,9 +469,13 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
     s0 = dot2(xw[4], kOnesF16x2, s0); s1 = dot2(xw[5], kOnesF16x2, s1);
     s0 = dot2(xw[6], kOnesF16x2, s0); s1 = dot2(xw[7], kOnesF16x2, s1);
     const int ch = m >> 8, ln = (m >> 2) & 63, gg = m & 3;
-    xpairs[(ch * 8 + 2 * gg) * 64 + ln] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-    xpairs[(ch * 8 + 2 * gg + 1) * 64 + ln] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
-    reinterpret_cast<float*>(gsum)[(ch * 64 + ln) * 4 + gg] = s0 + s1;
+    uint4* d0 = staged ? xpairs + (ch * 8 + 2 * gg) * 64 + ln : sink;
+    uint4* d1 = staged ? xpairs + (ch * 8 + 2 * gg + 1) * 64 + ln : sink + 1;
+    float* d2 = staged ? reinterpret_cast<float*>(gsum) + (ch * 64 + ln) * 4 + gg
+                       : reinterpret_cast<float*>(sink + 2);
+    *d0 = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+    *d1 = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+    *d2 = s0 + s1;
   }
   __syncthreads();
 
@@ -574,6 +595,8 @@ static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, fl
   const dim3 grid((unsigned)((groups + sp.S - 1) / sp.S));
   const size_t lds = f16_lds_bytes(sp.C, sp.S, R);
   const dim3 block(64 * sp.C * sp.S);
+  const int ct = sp.C <= 4 && sp.C != 3 ? sp.C : 0;
+  if ((int64_t)f16_stage_passes(ct) * block.x < (int64_t)sp.C * 256) return hipErrorInvalidConfiguration;
   if (sp.C == 1) {
     hipLaunchKernelGGL((k_gemv_f16<R, 1, 512, EPI>), grid, block, lds, s, m, K, x, y, sp);
   } else if (sp.C == 2) {
@@ -744,10 +767,10 @@ __device__ __forceinline__ float i8_epilogue(int64_t A, float s) {
   return (float)((a * (double)s) * 0x1p-24);
 }
 
-// LDS of the int8 matvec: x_q dwords [C][4][64] uint4, cross-wave sums
-// [C*S][R] int64.
+// LDS of the int8 matvec: x_q dwords [C][4][64] uint4, a sink uint4 for the
+// stores of threads with no group to stage, cross-wave sums [C*S][R] int64.
 __host__ __device__ inline size_t i8_lds_bytes(int C, int S, int R) {
-  return (size_t)C * 4 * 64 * 16 + (size_t)C * S * R * 8;
+  return (size_t)C * 4 * 64 * 16 + 16 + (size_t)C * S * R * 8;
 }
 
 // Same work split as the fp16 matvec.  The workgroup quantizes the
@@ -786,8 +809,9 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
                                                   Requant rq) {
   extern __shared__ uint4 lds[];
   const int C = CT ? CT : sp.C, S = sp.S;
-  uint4* xs = lds;                                            // [C][4][64]
-  int64_t* red = reinterpret_cast<int64_t*>(lds + C * 4 * 64);  // [C*S][R]
+  uint4* xs = lds;                                                // [C][4][64]
+  uint4* sink = lds + C * 4 * 64;                                 // [1]
+  int64_t* red = reinterpret_cast<int64_t*>(sink + 1);            // [C*S][R]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -802,34 +826,39 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
   const int64_t BK = K / kBlock;
   const int ngroups = (int)(K / 16);
 
-  // (1) loads: first pass of the activations (16 per thread), then weights
-  uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-  if (tid < ngroups) {
+  // (1) loads: the activations first (XP groups of 16 per thread, clamped),
+  //     then the weights; x stays first so that waiting for it does not
+  //     wait for the weights (loads complete in issue order).
+  constexpr int XP = f16_stage_passes(CT);
+  uint4 xa[XP], xb[XP];
+#pragma unroll
+  for (int p = 0; p < XP; ++p) {
+    const int m = tid + p * (int)blockDim.x;
+    const int gm = m < ngroups ? m : ngroups - 1;
     if (QUANT) {
-      xa = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)tid);
-      xb = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)tid + 8);
+      xa[p] = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm);
+      xb[p] = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm + 8);
     } else {
-      xa = *reinterpret_cast<const uint4*>(xq_in + 16 * (int64_t)tid);
+      xa[p] = *reinterpret_cast<const uint4*>(xq_in + 16 * (int64_t)gm);
+      xb[p] = make_uint4(0, 0, 0, 0);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
   uint4 w[R];
   uint16_t hs[R];
   load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs);
   __builtin_amdgcn_sched_barrier(0);
 
   // (2) stage: group m (weights 16m..16m+15) = group m % 4 of lane
-  //     (m / 4) % 64 of chunk m / 256
+  //     (m / 4) % 64 of chunk m / 256.  Every thread quantizes and stores;
+  //     one without a group stores into the sink (no branch for the x
+  //     loads to sink into).
   const float rs = 1.0f / s;
-  for (int m = tid; m < ngroups; m += blockDim.x) {
-    uint4 a4 = xa, b4 = xb;
-    if (m != tid) {
-      if (QUANT) {
-        a4 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)m);
-        b4 = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)m + 8);
-      } else {
-        a4 = *reinterpret_cast<const uint4*>(xq_in + 16 * (int64_t)m);
-      }
-    }
+#pragma unroll
+  for (int p = 0; p < XP; ++p) {
+    const int m = tid + p * (int)blockDim.x;
+    const bool staged = m < ngroups;
+    const uint4 a4 = xa[p], b4 = xb[p];
     int v[16];
     if (QUANT) {
       const uint32_t hw[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
@@ -849,7 +878,7 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
       dw[j] = ((uint32_t)v[j] & 0xFFu) | (((uint32_t)v[4 + j] & 0xFFu) << 8) |
               (((uint32_t)v[8 + j] & 0xFFu) << 16) | (((uint32_t)v[12 + j] & 0xFFu) << 24);
     const int ch = m >> 8, ln = (m >> 2) & 63, gg = m & 3;
-    xs[(ch * 4 + gg) * 64 + ln] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    *(staged ? xs + (ch * 4 + gg) * 64 + ln : sink) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
   }
   __syncthreads();
 
@@ -916,8 +945,13 @@ static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, con
   const int64_t grid = (groups + sp.S - 1) / sp.S;
   const size_t lds = i8_lds_bytes(sp.C, sp.S, R);
   const dim3 g((unsigned)grid), b(64 * sp.C * sp.S);
+  const int ct = sp.C <= 4 && sp.C != 3 ? sp.C : 0;
+  if ((int64_t)f16_stage_passes(ct) * b.x < K / 16) return hipErrorInvalidConfiguration;
   if (sp.C == 1)
     hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 1, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, y,
+                       partials, sp, rq);
+  else if (sp.C == 2)
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 2, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, y,
                        partials, sp, rq);
   else if (sp.C == 4)
     hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 4, 1024, REQUANT>), g, b, lds, st, m, K, x, xq, s,
