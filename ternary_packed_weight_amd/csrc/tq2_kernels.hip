@@ -561,19 +561,21 @@ static int device_cus() {
   return cus;
 }
 
-// Waves per workgroup: C chunk-waves for each of S row groups.  8 waves when
-// C divides 8, except K = 16384 (C = 4), where 16-wave workgroups halve the
-// activation staging per row and measured faster on MI355X.
-static Split pick_split(int64_t K) {
+// Waves per workgroup: C chunk-waves for each of S row groups (measured on
+// MI355X).  fp16, one chunk (K <= 4096): 4-wave workgroups.  Otherwise 8
+// waves when C divides 8, except K = 16384 (C = 4), where 16-wave workgroups
+// halve the activation staging per row.
+static Split pick_split(int64_t K, bool fp16) {
   const int C = (int)chunks_of(K);
   Split sp;
   sp.C = C;
-  sp.S = C == 4 ? 4 : (C >= 8 ? 1 : 8 / C);
+  sp.S = (fp16 && C == 1) ? 4 : (C == 4 ? 4 : (C >= 8 ? 1 : 8 / C));
   return sp;
 }
 
-// Rows per wave (measured on MI355X): both matvecs do best with ~16 waves
-// per CU, i.e. as many rows per wave (up to rmax) as still give that many.
+// Rows per wave (measured on MI355X): as many rows per wave (up to rmax) as
+// still give waves_per_cu waves per CU; the fp16 matvec does best with 8
+// waves per CU for one chunk and 16 otherwise, the int8 matvec with 16.
 static int pick_rows_per_wave(int64_t rows, int C, int waves_per_cu, int rmax) {
   const int64_t want_waves = (int64_t)device_cus() * waves_per_cu;
   for (int R = rmax; R > 2; R /= 2) {
@@ -589,7 +591,7 @@ static hipError_t set_lds_cap(const void* fn) {
 template <int R, int EPI>
 static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
                                hipStream_t s) {
-  const Split sp = pick_split(K);
+  const Split sp = pick_split(K, true);
   // PAIR rows: R/2 outputs per row group, each reading one gate and one up row
   const int64_t groups = EPI == kSiluMul ? (m.row_begin[1] + R / 2 - 1) / (R / 2) : (m.rows + R - 1) / R;
   const dim3 grid((unsigned)((groups + sp.S - 1) / sp.S));
@@ -615,9 +617,11 @@ static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, fl
   return hipGetLastError();
 }
 
+static int f16_waves_per_cu(int64_t K) { return chunks_of(K) == 1 ? 8 : 16; }
+
 hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
                            hipStream_t s) {
-  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 16, 8)) {
+  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), f16_waves_per_cu(K), 8)) {
     case 8: return run_gemv_f16<8, kStoreF32>(m, K, x, y, s);
     case 4: return run_gemv_f16<4, kStoreF32>(m, K, x, y, s);
     default: return run_gemv_f16<2, kStoreF32>(m, K, x, y, s);
@@ -626,7 +630,7 @@ hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float*
 
 hipError_t launch_gemv_silu_mul(const MatSet& m, int64_t K, const uint16_t* x, float* h,
                                 hipStream_t s) {
-  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), 16, 8)) {
+  switch (pick_rows_per_wave(m.rows, (int)chunks_of(K), f16_waves_per_cu(K), 8)) {
     case 8: return run_gemv_f16<8, kSiluMul>(m, K, x, h, s);
     case 4: return run_gemv_f16<4, kSiluMul>(m, K, x, h, s);
     default: return run_gemv_f16<2, kSiluMul>(m, K, x, h, s);
@@ -940,7 +944,7 @@ template <int R, bool QUANT, bool PARTIALS, bool REQUANT>
 static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
                               float s, float* y, int32_t* partials, const Requant& rq,
                               hipStream_t st) {
-  const Split sp = pick_split(K);
+  const Split sp = pick_split(K, false);
   const int64_t groups = (m.rows + R - 1) / R;
   const int64_t grid = (groups + sp.S - 1) / sp.S;
   const size_t lds = i8_lds_bytes(sp.C, sp.S, R);
