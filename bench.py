@@ -192,6 +192,82 @@ def run_probes(torch, nbytes=1 << 30):
     return {"read_bytes": nbytes, "fill_bytes": nbytes // 4}
 
 
+CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed with cache rotation
+    ("c0 q/k-like 256x4096 fp16", 256, 4096, "f16", 1000),
+    ("c1 q/o 4096x4096 fp16", 4096, 4096, "f16", 1001),
+    ("c2 fused gate+up 2x16384x4096 fp16", 16384, 4096, "gate_up", 1003),
+    ("c3 down 4096x16384 int8 (fused quantize)", 4096, 16384, "i8", 1004),
+]
+ROTATION_BYTES = 1.1e9  # > the 256 MB Infinity Cache: every timed call streams from HBM
+
+
+def time_configs(torch, tq2, synth, reps=5):
+    """Per-call time of each single-call configuration: C rotating copies of
+    the weights (>= 1.1 GB in all), up to 400 back-to-back calls captured as
+    one graph, median over `reps` replays.  Beside it, a read-only 16-byte
+    stream kernel, one dispatch per call reading the call's weight bytes from
+    a rotating pool of the same size: the achievable ceiling at that size,
+    dispatch floor included."""
+    import numpy as np
+    probe = ctypes.CDLL(os.path.join(ROOT, "ternary_packed_weight_amd", "libtq2probe.so"))
+    probe.tq2probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_void_p]
+    probe.tq2probe_read.restype = ctypes.c_int32
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    out = {}
+    for label, N, K, kind, seed in CONFIGS:
+        nmat = 2 if kind == "gate_up" else 1
+        mats = []
+        xs = None
+        for i in range(nmat):
+            q, d, x = synth.torch_problem(seed + 100 * i, N, K)
+            W = d.float().repeat_interleave(256, dim=1) * (q.float() - 1.0)
+            c, s, _ = tq2.tq2_pack(W)
+            del W, q, d
+            mats.append((c, s))
+            xs = x if xs is None else xs
+        nbytes = nmat * (N * K * 66 // 256 + 4 * N) + 2 * K  # x read once
+        ncopy = max(2, int(np.ceil(ROTATION_BYTES / nbytes)))
+        copies = [[(c.clone(), s.clone()) for (c, s) in mats] for _ in range(ncopy)]
+        del mats
+        ncall = min(ncopy, 400)
+        y = torch.empty(nmat * N, dtype=torch.float32, device="cuda")
+        sc = float(xs.float().abs().max() / 100)
+        if kind == "f16":
+            calls = [lambda j=j: tq2.tq2_gemv(copies[j][0][0], copies[j][0][1], xs, y=y) for j in range(ncall)]
+        elif kind == "gate_up":
+            calls = [lambda j=j: tq2.tq2_gemv_gate_up(copies[j][0][0], copies[j][0][1], copies[j][1][0],
+                                                      copies[j][1][1], xs, y=y.view(2, N)) for j in range(ncall)]
+        else:
+            calls = [lambda j=j: tq2.tq2_gemv_i8(copies[j][0][0], copies[j][0][1], xs, sc, y=y)
+                     for j in range(ncall)]
+        g = capture(torch, calls)
+        us = float(np.median([time_graph(torch, g, 1) / ncall for _ in range(reps)]))
+        del g, calls, copies
+        torch.cuda.empty_cache()
+
+        rb = (nmat * N * K * 66 // 256 + 255) // 256 * 256  # the call's weight bytes
+        pool = torch.ones(ncopy * rb, dtype=torch.uint8, device="cuda")
+        st = ctypes.c_void_p
+        rcalls = [lambda j=j: probe.tq2probe_read(st(pool.data_ptr() + j * rb), rb, st(sink.data_ptr()), 2048,
+                                                  st(torch.cuda.current_stream().cuda_stream))
+                  for j in range(ncall)]
+        g = capture(torch, rcalls)
+        us_rd = float(np.median([time_graph(torch, g, 1) / ncall for _ in range(reps)]))
+        del g, rcalls, pool
+        torch.cuda.empty_cache()
+        gbs = nbytes / us / 1e3
+        rd_gbs = rb / us_rd / 1e3
+        out[label] = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1),
+                      "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+                      "read_probe_us": round(us_rd, 3), "read_probe_GB_s": round(rd_gbs, 1),
+                      "pct_of_read_probe": round(100 * gbs / rd_gbs, 1),
+                      "bytes_per_call": int(nbytes), "rotation_copies": ncopy}
+        log(f"{label}: {us:.2f} us/call, {gbs:.1f} GB/s ({gbs / PEAK_HBM_GBS:.1%}); "
+            f"read probe {us_rd:.2f} us, {rd_gbs:.1f} GB/s")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +276,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg (and its parity gate)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--probes", action="store_true", help="also run the byte-counter calibration kernels")
+    ap.add_argument("--no-configs", action="store_true", help="skip the single-call configuration timings")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -257,6 +334,10 @@ def main():
         torch.cuda.synchronize()
         run_probes(torch)
 
+    configs = None
+    if not args.no_configs:
+        configs = time_configs(torch, tq2, synth)
+
     cpu, parity = None, None
     if not args.no_cpu:
         ys0 = [stack[i]["y"].cpu().numpy() for i in range(len(PROJ))]
@@ -276,6 +357,7 @@ def main():
         "steps_per_s": round(1e6 / us_step, 1),
         "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
         "roofline": roofline,
+        "configs": configs,
         "cpu_baseline": cpu,
         "parity": parity,
     }
