@@ -371,6 +371,12 @@ struct Split {
 
 __host__ __device__ constexpr int f16_stage_passes(int CT) { return CT ? 1 : 4; }
 
+// 16 bytes at byte offset `off` of a buffer; zeros past its end.
+__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, int off) {
+  const v4u v = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 
 // LDS of the fp16 matvec: x pairs [C][8][64] uint4, group sums [C][64] float4,
 // a sink [3] uint4 for the stores of threads with no group to stage,
@@ -419,14 +425,17 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   //     the staging (and the barrier) until every weight had arrived.
   // staging passes over the C*256 groups: the launcher guarantees
   // XP * blockDim >= C*256 (one pass for C <= 4, four for the runtime-C form)
+  //     x is read through a buffer descriptor of exactly K elements, so the
+  //     groups past K (a partial last chunk) come back as zeros, with no
+  //     masking in the staging.
   constexpr int XP = f16_stage_passes(CT);
   uint4 xa[XP], xb[XP];
+  const __amdgpu_buffer_rsrc_t xr = rsrc(x, (uint32_t)(K * 2));
 #pragma unroll
   for (int p = 0; p < XP; ++p) {
     const int m = tid + p * (int)blockDim.x;
-    const int gm = m < ngroups ? m : ngroups - 1;
-    xa[p] = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm);
-    xb[p] = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm + 8);
+    xa[p] = load_b128(xr, 32 * m);
+    xb[p] = load_b128(xr, 32 * m + 16);
   }
   __builtin_amdgcn_sched_barrier(0);
   constexpr bool PAIR = EPI == kSiluMul;
@@ -448,21 +457,17 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
     const int m = tid + p * (int)blockDim.x;
     const bool staged = m < C * 256;
     const uint4 a4 = xa[p], b4 = xb[p];
-    const uint32_t z = m < ngroups ? 0xFFFFFFFFu : 0u;
-    const uint32_t xw[8] = {a4.x & z, a4.y & z, a4.z & z, a4.w & z,
-                            b4.x & z, b4.y & z, b4.z & z, b4.w & z};
+    const uint32_t xw[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+    // pair (x[16m + e0], x[16m + e1]): one byte permute of the two dwords
+    // holding them, low halves (selector 0x05040100) or high (0x07060302)
     uint32_t pr[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t a = xw[j >> 1], b = xw[4 + (j >> 1)];
       const uint32_t cc = xw[2 + (j >> 1)], d = xw[6 + (j >> 1)];
-      if (j & 1) {
-        pr[2 * j + 0] = (a >> 16) | (b & 0xFFFF0000u);
-        pr[2 * j + 1] = (cc >> 16) | (d & 0xFFFF0000u);
-      } else {
-        pr[2 * j + 0] = (a & 0xFFFFu) | (b << 16);
-        pr[2 * j + 1] = (cc & 0xFFFFu) | (d << 16);
-      }
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      pr[2 * j + 0] = __builtin_amdgcn_perm(b, a, sel);
+      pr[2 * j + 1] = __builtin_amdgcn_perm(d, cc, sel);
     }
     float s0 = dot2(xw[0], kOnesF16x2, 0.0f), s1 = dot2(xw[1], kOnesF16x2, 0.0f);
     s0 = dot2(xw[2], kOnesF16x2, s0); s1 = dot2(xw[3], kOnesF16x2, s1);
@@ -835,15 +840,17 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
   //     wait for the weights (loads complete in issue order).
   constexpr int XP = f16_stage_passes(CT);
   uint4 xa[XP], xb[XP];
+  // range-checked: groups past K load as zeros (and quantize to 0)
+  const __amdgpu_buffer_rsrc_t xr =
+      QUANT ? rsrc(x, (uint32_t)(K * 2)) : rsrc(xq_in, (uint32_t)K);
 #pragma unroll
   for (int p = 0; p < XP; ++p) {
     const int m = tid + p * (int)blockDim.x;
-    const int gm = m < ngroups ? m : ngroups - 1;
     if (QUANT) {
-      xa[p] = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm);
-      xb[p] = *reinterpret_cast<const uint4*>(x + 16 * (int64_t)gm + 8);
+      xa[p] = load_b128(xr, 32 * m);
+      xb[p] = load_b128(xr, 32 * m + 16);
     } else {
-      xa[p] = *reinterpret_cast<const uint4*>(xq_in + 16 * (int64_t)gm);
+      xa[p] = load_b128(xr, 16 * m);
       xb[p] = make_uint4(0, 0, 0, 0);
     }
   }
