@@ -14,6 +14,7 @@ Functions (each cites its passage in tq2_oracle.c):
   gemv_i8(codes, scales, N, K, x_bits, s) -> y
   requant_i8(y, s_out)         -> y_q, y_deq
   silu_mul(g, u)               -> h (fp64)
+  gemm(codes, scales, N, K, X_bits[M][K]) -> Y[M][N] (one matvec per token)
   half_to_float(bits), float_to_half(value)
 """
 import ctypes
@@ -56,6 +57,8 @@ def _lib():
         lib.oracle_requant_i8.restype = None
         lib.oracle_silu_mul.argtypes = [P, P, I64, P]
         lib.oracle_silu_mul.restype = None
+        lib.oracle_gemm.argtypes = [P, P, I64, I64, P, I64, P]
+        lib.oracle_gemm.restype = None
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         _LIB = lib
@@ -172,3 +175,15 @@ def silu_mul(g, u):
     h = np.empty(g.size, np.float64)
     _lib().oracle_silu_mul(pg, pu, g.size, h.ctypes.data_as(ctypes.c_void_p))
     return h
+
+
+def gemm(codes, scales, N, K, X_bits):
+    _shape_check(N, K)
+    codes, pc = _c(codes, np.uint8)
+    scales, ps = _c(scales, np.uint16)
+    X_bits, px = _c(X_bits, np.uint16)
+    M = X_bits.size // K
+    assert X_bits.size == M * K and M >= 1
+    Y = np.empty((M, N), np.float32)
+    _lib().oracle_gemm(pc, ps, N, K, px, M, Y.ctypes.data_as(ctypes.c_void_p))
+    return Y

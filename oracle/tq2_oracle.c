@@ -268,3 +268,11 @@ void oracle_silu_mul(const float *g, const float *u, int64_t N, double *h)
         h[n] = v / (1.0 + exp(-v)) * (double)u[n];
     }
 }
+
+/* ---- several tokens: Y[m] = W X[m] for each token m, the matvec above
+ * applied token by token (the page's prefill runs one matvec per token). */
+void oracle_gemm(const uint8_t *codes, const uint16_t *scales, int64_t N,
+                 int64_t K, const uint16_t *X, int64_t M, float *Y)
+{
+    for (int64_t m = 0; m < M; ++m) oracle_gemv(codes, scales, N, K, X + m * K, Y + m * N);
+}

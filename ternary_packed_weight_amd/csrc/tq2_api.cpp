@@ -281,4 +281,29 @@ int32_t tq2_gemv_i8_requant(const uint8_t* codes, const uint16_t* scales, int64_
                    y_deq, stream);
 }
 
+size_t tq2_gemm_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+  if (check_shape(N, K, TQ2_MAX_K) != TQ2_OK || M < 1 || M > TQ2_MAX_TOKENS) return (size_t)-1;
+  return tq2::gemm_workspace_bytes(N, K, M);
+}
+
+int32_t tq2_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const uint16_t* x,
+                 int64_t M, float* y, void* ws, size_t ws_bytes, tq2_stream_t stream) {
+  TQ2_TRY(check_shape(N, K, TQ2_MAX_K));
+  TQ2_TRY(check_weights(codes, scales));
+  if (M < 1 || M > TQ2_MAX_TOKENS || !x || !y) return TQ2_ERR_ARG;
+  if (M * N > ((int64_t)1 << 40)) return TQ2_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 4)) return TQ2_ERR_ALIGN;
+  const size_t need = tq2::gemm_workspace_bytes(N, K, M);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return TQ2_ERR_WORKSPACE;
+  const size_t xb = (size_t)(M * K) * 2, yb = (size_t)(M * N) * 4;
+  const size_t cb = (size_t)(N * (K / 4)), sb = (size_t)(N * (K / TQ2_BLOCK)) * 2;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, codes, cb) || overlaps(y, yb, scales, sb))
+    return TQ2_ERR_ARG;
+  if (overlaps(ws, need, x, xb) || overlaps(ws, need, y, yb) || overlaps(ws, need, codes, cb) ||
+      overlaps(ws, need, scales, sb))
+    return TQ2_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return hip_status(tq2::launch_gemm(codes, scales, N, K, x, M, y, ws, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -642,6 +642,275 @@ hipError_t launch_gemv_silu_mul(const MatSet& m, int64_t K, const uint16_t* x, f
   }
 }
 
+// -------------------------------------------- small-M batched matvec (MFMA)
+//
+// Y[M][N] = X[M][K] . W^T for a few tokens at once (prefill, speculative
+// decode): the weight stream is paid once for all M tokens.  Page "BitCPM
+// ternary (1.58-bit)", kernel paragraph, applied per token.
+//
+// A 16 x 32 tile of the masked codes is the A operand of
+// v_mfma_f32_16x16x32_f16 (the same subnormal binary16 decode as the
+// matvec); the B operand carries the x values of 16 tokens, one per column,
+// so the matrix cores do useful work in every column.  Lane (G = l/16,
+// i = l%16) supplies row i's codes at k-slots 8G..8G+7 and token i's x
+// values at the same slots, and receives D[rows 4G..4G+3][token i].
+//
+//   prep   : X -> ready B operands (pairs scaled by 4^-j, the j-th mask
+//            position) and block zero points -sum(x)*2^-24, in the workspace;
+//   gemm   : a wave owns U row groups (16U rows) and a K-split; per 256-block
+//            step, 8 MFMAs per row group starting from the zero point, then
+//            acc += d_row * D;
+//   reduce : when K is split, the split partials are added in split order.
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kTok = 16;        // tokens per tile (MFMA columns)
+constexpr int kTileRows16 = 16;  // rows per MFMA tile
+
+// Prep: one thread per (token of the padded tile set, 16-weight group).
+// xb[tt][K/64][8][16] uint4, operand 2j+h of segment s, token i, holding for
+// g = 0..3 the pair (x[64s+16g+4h+j], x[64s+16g+8+4h+j]) * 4^-j;
+// zt[tt][K/256][16] float.
+__global__ __launch_bounds__(256) void k_gemm_prep(const uint16_t* __restrict__ x, int64_t M,
+                                                   int64_t K, int64_t Mpad,
+                                                   uint4* __restrict__ xb, float* __restrict__ zt) {
+  const int64_t ng = K / 16;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = id < Mpad * ng;  // the grid is a multiple of 16 threads; see below
+  const int64_t tok = live ? id / ng : 0;
+  const int64_t g16 = live ? id - tok * ng : 0;
+  uint32_t xw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (live && tok < M) {
+    const uint4 a = *reinterpret_cast<const uint4*>(x + tok * K + 16 * g16);
+    const uint4 b = *reinterpret_cast<const uint4*>(x + tok * K + 16 * g16 + 8);
+    xw[0] = a.x; xw[1] = a.y; xw[2] = a.z; xw[3] = a.w;
+    xw[4] = b.x; xw[5] = b.y; xw[6] = b.z; xw[7] = b.w;
+  }
+  const int64_t tt = tok / kTok, ti = tok % kTok;
+  const int64_t seg = g16 >> 2, g = g16 & 3;
+  const int64_t nseg = K / 64;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e0 = 4 * h + j, e1 = 8 + 4 * h + j;  // x[16 g16 + e] is half e&1 of xw[e>>1]
+      const uint32_t sel = ((e0 & 1) ? 0x0302u : 0x0100u) | ((e1 & 1) ? 0x07060000u : 0x05040000u);
+      uint32_t pr = __builtin_amdgcn_perm(xw[e1 >> 1], xw[e0 >> 1], sel);
+      if (j) {
+        const half2v sc = {(_Float16)(1.0f / (float)(1 << (2 * j))), (_Float16)(1.0f / (float)(1 << (2 * j)))};
+        pr = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr) * sc);
+      }
+      if (live)
+        reinterpret_cast<uint32_t*>(xb + ((tt * nseg + seg) * 8 + (2 * j + h)) * kTok + ti)[g] = pr;
+    }
+  }
+  float s0 = dot2(xw[0], kOnesF16x2, 0.0f), s1 = dot2(xw[1], kOnesF16x2, 0.0f);
+  s0 = dot2(xw[2], kOnesF16x2, s0); s1 = dot2(xw[3], kOnesF16x2, s1);
+  s0 = dot2(xw[4], kOnesF16x2, s0); s1 = dot2(xw[5], kOnesF16x2, s1);
+  s0 = dot2(xw[6], kOnesF16x2, s0); s1 = dot2(xw[7], kOnesF16x2, s1);
+  float bs = s0 + s1;  // the 16 groups of one block are 16 consecutive threads (one DPP row)
+  bs += dpp_f32<0x128>(bs);
+  bs += dpp_f32<0x124>(bs);
+  bs += dpp_f32<0x122>(bs);
+  bs += dpp_f32<0x121>(bs);
+  if (live && (g16 & 15) == 0) zt[(tt * (K / kBlock) + (g16 >> 4)) * kTok + ti] = -ldexpf(bs, -24);
+}
+
+struct GemmArgs {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint4* xb;
+  const float* zt;
+  float* out;         // y[M][N], or the split partials [splits][M][N]
+  int64_t N, K, M;
+  int32_t steps_per_split;
+};
+
+// Wave: U row groups x one K-split x one token tile.  Workgroup: S waves
+// (S row sets of the same split and tile).
+template <int U, int T>
+__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4, i = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = blockDim.x >> 6;
+  const int rset = (int)blockIdx.x * S + wave;
+  const int split = blockIdx.y, tt = blockIdx.z;
+  const int64_t row_bytes = a.K / 4, BK = a.K / kBlock, nseg = a.K / 64;
+  const int s_begin = split * a.steps_per_split;
+  const int s_end = (int)((int64_t)s_begin + a.steps_per_split < BK ? s_begin + a.steps_per_split : BK);
+
+  // per row group: scalar descriptors over its valid rows (zeros past N)
+  __amdgpu_buffer_rsrc_t rc[U], rs[U];
+  int valid[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int gi = rset * U + u;
+    int v = (int)(a.N - (int64_t)gi * kTileRows16);
+    v = v < 0 ? 0 : (v > kTileRows16 ? kTileRows16 : v);
+    v = __builtin_amdgcn_readfirstlane(v);
+    valid[u] = v;
+    const int64_t r0 = v > 0 ? (int64_t)gi * kTileRows16 : 0;
+    rc[u] = rsrc(a.codes + r0 * row_bytes, (uint32_t)(v * row_bytes));
+    rs[u] = rsrc(a.scales + r0 * BK, (uint32_t)(v * BK * 2));
+  }
+
+  v4f acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int s0 = s_begin; s0 < s_end; s0 += T) {
+    // issue, in this order (loads complete in issue order): the B operands
+    // and zero points of up to T steps (L2), then the code words (HBM), then
+    // the scales.  Steps past the split read zeros.
+    uint4 bo[T][8];
+    float z[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int s = s0 + t < s_end ? s0 + t : s_begin;  // in range; unused when past the split
+      const uint4* bp = a.xb + ((int64_t)tt * nseg + 4 * s + G) * 8 * kTok + i;
+#pragma unroll
+      for (int o = 0; o < 8; ++o) bo[t][o] = bp[o * kTok];
+      z[t] = a.zt[((int64_t)tt * BK + s) * kTok + i];
+    }
+    uint4 w[T][U];
+    uint16_t d[T][U][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int s = s0 + t;
+      const bool ok = s < s_end;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t off = ok ? (uint32_t)(i * row_bytes + 64 * s + 16 * G) : 0x7FFFFFF0u;
+        const v4u v = __builtin_bit_cast(
+            v4u, __builtin_amdgcn_raw_buffer_load_b128(rc[u], (int)off, 0, kNonTemporal));
+        w[t][u] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int s = s0 + t;
+      const bool ok = s < s_end;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t so = ok ? (uint32_t)(((4 * G + r) * BK + s) * 2) : 0x7FFFFFF0u;
+          d[t][u][r] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs[u], (int)so, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (s0 + t >= s_end) break;  // uniform
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t v[4] = {w[t][u].x, w[t][u].y, w[t][u].z, w[t][u].w};
+        uint32_t v8[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) v8[g] = v[g] >> 8;
+        v4f D = v4f{z[t], z[t], z[t], z[t]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t mask = 0x00030003u << (2 * j);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t* src = h ? v8 : v;
+            const uint4 av = make_uint4(src[0] & mask, src[1] & mask, src[2] & mask, src[3] & mask);
+            D = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av),
+                                                       __builtin_bit_cast(v8h, bo[t][2 * j + h]), D, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[u][r] = __builtin_fmaf(half_to_float(d[t][u][r]), D[r], acc[u][r]);
+      }
+    }
+  }
+
+  // lane (G, i): rows 4G..4G+3 of each group, token tt*16 + i
+  const int64_t tok = (int64_t)tt * kTok + i;
+  if (tok >= a.M) return;
+  float* o = a.out + ((int64_t)split * a.M + tok) * a.N;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t gi = (int64_t)rset * U + u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * G + r < valid[u]) o[gi * kTileRows16 + 4 * G + r] = ldexpf(acc[u][r], 24);
+  }
+}
+
+// y = sum over splits of the partials, in split order.
+__global__ __launch_bounds__(256) void k_gemm_reduce(const float* __restrict__ part, int splits,
+                                                     int64_t MN, float* __restrict__ y) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= MN) return;
+  float s = part[id];
+  for (int p = 1; p < splits; ++p) s += part[(int64_t)p * MN + id];
+  y[id] = s;
+}
+
+GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
+  GemmPlan p;
+  p.U = 4;
+  p.T = 2;
+  p.S = 4;
+  p.mt = (M + kTok - 1) / kTok;
+  const int64_t steps = K / kBlock;
+  const int64_t rsets = ((N + kTileRows16 - 1) / kTileRows16 + p.U - 1) / p.U;
+  const int64_t wgs = (rsets + p.S - 1) / p.S;
+  const int64_t want = 2LL * device_cus();  // workgroups
+  int64_t splits = (want + wgs * p.mt - 1) / (wgs * p.mt);
+  if (splits < 1) splits = 1;
+  if (splits > steps) splits = steps;
+  int64_t sps = (steps + splits - 1) / splits;
+  sps = (sps + p.T - 1) / p.T * p.T;
+  p.splits = (steps + sps - 1) / sps;
+  p.steps_per_split = sps;
+  p.wgs = wgs;
+  p.xb_bytes = p.mt * kTok * K * 2;
+  p.zt_bytes = p.mt * kTok * steps * 4;
+  p.part_bytes = p.splits > 1 ? p.splits * M * N * 4 : 0;
+  return p;
+}
+
+size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+  const GemmPlan p = plan_gemm(N, K, M);
+  return (size_t)(p.xb_bytes + p.zt_bytes + p.part_bytes);
+}
+
+hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                       const uint16_t* x, int64_t M, float* y, void* ws, hipStream_t st) {
+  const GemmPlan p = plan_gemm(N, K, M);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  uint4* xb = reinterpret_cast<uint4*>(wsb);
+  float* zt = reinterpret_cast<float*>(wsb + p.xb_bytes);
+  float* part = reinterpret_cast<float*>(wsb + p.xb_bytes + p.zt_bytes);
+  const int64_t prep_threads = p.mt * kTok * (K / 16);
+  hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, x, M, K,
+                     p.mt * kTok, xb, zt);
+  GemmArgs a;
+  a.codes = codes;
+  a.scales = scales;
+  a.xb = xb;
+  a.zt = zt;
+  a.out = p.splits > 1 ? part : y;
+  a.N = N;
+  a.K = K;
+  a.M = M;
+  a.steps_per_split = (int32_t)p.steps_per_split;
+  hipLaunchKernelGGL((k_gemm_mfma<4, 2>), dim3((unsigned)p.wgs, (unsigned)p.splits, (unsigned)p.mt),
+                     dim3(64 * p.S), 0, st, a);
+  if (p.splits > 1) {
+    const int64_t MN = M * N;
+    hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, part,
+                       (int)p.splits, MN, y);
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ int8 path
 // Static int8 activation quantization (page "gemma4 wNa8o8 requires int8
 // activations"): x_q = clamp(rint(x / s), -128, 127) with x/s one IEEE fp32

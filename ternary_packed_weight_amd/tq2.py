@@ -59,13 +59,17 @@ _lib.tq2_gemv_gate_up_silu.argtypes = [_P, _P, _P, _P, _I64, _I64, _P, _P, _P, _
 _lib.tq2_gemv_gate_up_silu.restype = _I32
 _lib.tq2_gemv_i8_requant.argtypes = [_P, _P, _I64, _I64, _P, _F, _F, _P, _P, _P, _SZ, _P]
 _lib.tq2_gemv_i8_requant.restype = _I32
+_lib.tq2_gemm_workspace_bytes.argtypes = [_I64, _I64, _I64]
+_lib.tq2_gemm_workspace_bytes.restype = _SZ
+_lib.tq2_gemm.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]
+_lib.tq2_gemm.restype = _I32
 
 TQ2_OK = 0
 TQ2_OP_GEMV, TQ2_OP_GATE_UP, TQ2_OP_GEMV_I8, TQ2_OP_GEMV_I8Q = 0, 1, 2, 3
 EXPORTED = ("tq2_abi_version", "tq2_status_string", "tq2_codes_bytes", "tq2_scales_bytes",
             "tq2_workspace_bytes", "tq2_pack", "tq2_dequant", "tq2_gemv", "tq2_gemv_gate_up",
             "tq2_quantize_i8", "tq2_gemv_i8q", "tq2_gemv_i8", "tq2_gemv_fused", "tq2_gemv_i8_fused",
-            "tq2_gemv_gate_up_silu", "tq2_gemv_i8_requant")
+            "tq2_gemv_gate_up_silu", "tq2_gemv_i8_requant", "tq2_gemm_workspace_bytes", "tq2_gemm")
 
 
 class Tq2Error(RuntimeError):
@@ -282,3 +286,26 @@ def tq2_gemv_i8_requant(codes, scales, x, s_in, s_out, y_q=None, y_deq=None, wan
         _ptr(codes), _ptr(scales), N, K, _ptr(x), float(s_in), float(s_out), _ptr(y_q), _ptr(y_deq),
         _ptr(ws), wsb, _stream(stream)))
     return y_q, y_deq
+
+
+def tq2_gemm_workspace_bytes(N, K, M):
+    return int(_lib.tq2_gemm_workspace_bytes(N, K, M))
+
+
+def tq2_gemm(codes, scales, x, y=None, ws=None, stream=None):
+    """Y[M][N] = X[M][K] W^T for x of shape [M, K] (fp16); allocates the
+    workspace when none is given."""
+    N, K = _shape(codes, scales)
+    _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [M, {K}]")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty(M, N, dtype=torch.float32, device=codes.device)
+    need = tq2_gemm_workspace_bytes(N, K, M)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=codes.device)
+    wsb = ws.numel() * ws.element_size()
+    _check("tq2_gemm", _lib.tq2_gemm(_ptr(codes), _ptr(scales), N, K, _ptr(x), M, _ptr(y), _ptr(ws), wsb,
+                                      _stream(stream)))
+    return y

@@ -160,3 +160,24 @@ def test_error_paths_fused_and_epilogues(tq2):
         None, 0, None)
     assert rq(s_out=0.0) == 5 and rq(s_out=float("nan")) == 5 and rq(s_in=-1.0) == 5
     assert rq(yq=0) == 1 and rq(yd=A + 2 ** 27 + 2) == 3 and rq(yd=y) == 1
+
+
+@no_gpu
+def test_error_paths_gemm(tq2):
+    lib = tq2.lib()
+    N, K, M = 4096, 4096, 16
+    need = lib.tq2_gemm_workspace_bytes(N, K, M)
+    assert 0 < need < 2 ** 40
+    assert lib.tq2_gemm_workspace_bytes(N, 1000, M) == ctypes.c_size_t(-1).value
+    assert lib.tq2_gemm_workspace_bytes(N, K, 0) == ctypes.c_size_t(-1).value
+    c, s = A, A + 2 ** 24
+    x, y, ws = A + 2 ** 26, A + 2 ** 27, A + 2 ** 28
+
+    def g(xx=x, MM=M, yy=y, w=ws, wb=need, KK=K):
+        return lib.tq2_gemm(P(c), P(s), N, KK, P(xx), MM, P(yy), P(w), wb, None)
+
+    assert g(MM=0) == 1 and g(MM=65537) == 1 and g(KK=1000) == 2
+    assert g(xx=x + 2) == 3 and g(yy=y + 2) == 3
+    assert g(w=0) == 4 and g(wb=need - 1) == 4 and g(w=ws + 16) == 4
+    assert g(yy=x) == 1                      # y overlapping x
+    assert g(w=y) == 4                       # workspace overlapping y

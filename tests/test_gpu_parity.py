@@ -419,3 +419,46 @@ def test_int8_requant_bit_exact(tq2, N, K, div_in, s_out):
     assert np.array_equal(yd.cpu().numpy().view(np.uint32), yd_ref.view(np.uint32))
     if s_out == 0.002:
         assert np.count_nonzero(np.abs(yq_ref.astype(np.int32)) >= 127) > 0   # saturation exercised
+
+
+# ------------------------------------------------------------ several tokens
+
+GEMM_SHAPES = [(256, 4096, 16), (33, 768, 5), (4096, 4096, 2), (1000, 1280, 17), (64, 256, 1),
+               (4096, 16384, 16), (16384, 4096, 8), (7, 65280, 3), (300, 4352, 33)]
+
+
+@pytest.mark.parametrize("N,K,M", GEMM_SHAPES)
+def test_gemm_parity(tq2, N, K, M):
+    """Y = X W^T for M tokens against the oracle (one matvec per token), with
+    the fp16-path tolerance per output; tiles of 16 tokens, ragged N and K
+    not a multiple of the split all covered."""
+    _, c, s, _ = _packed(1800 + N + M, N, K)
+    g = synth.rng(1900 + M)
+    X = np.stack([synth.activations(g, K) for _ in range(M)])
+    dc, ds = _to_dev(c, s)
+    Xd = torch.from_numpy(np.ascontiguousarray(X, np.float16)).to(DEV)
+    Y = tq2.tq2_gemm(dc, ds, Xd)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(c, s, N, K, synth.bits(X))
+    Yc = Y.cpu().numpy()
+    for m in range(M):
+        _check_f16(Yc[m], ref[m], _tol(s, X[m], N, K))
+
+
+def test_gemm_token_independence_and_determinism(tq2):
+    """A token's output does not depend on the other tokens of the call, and
+    repeated calls are bitwise identical (split partials added in order)."""
+    N, K = 4096, 16384
+    _, c, s, _ = _packed(1950, N, K)
+    g = synth.rng(1951)
+    X = np.stack([synth.activations(g, K) for _ in range(16)])
+    dc, ds = _to_dev(c, s)
+    Xd = torch.from_numpy(np.ascontiguousarray(X, np.float16)).to(DEV)
+    Y1 = tq2.tq2_gemm(dc, ds, Xd)
+    Y2 = tq2.tq2_gemm(dc, ds, Xd)
+    Y3 = tq2.tq2_gemm(dc, ds, Xd[5:6].contiguous())
+    Yv = tq2.tq2_gemv(dc, ds, Xd[5].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+    assert torch.equal(Y1[5], Y3[0])
+    _check_f16(Y1[5].cpu().numpy(), Yv.cpu().numpy().astype(np.float64), 2 * _tol(s, X[5], N, K))

@@ -385,3 +385,27 @@ def test_silu_mul_reference():
     # silu(v) -> v as v -> inf and -> -v e^v as v -> -inf
     assert abs(h[3] - 30.0) < 1e-11 and abs(h[4] + 30.0 * math.exp(-30.0)) < 1e-20
     assert h[6] < 0 and abs(h[6]) < 1e-290
+
+
+# ------------------------------------------------------------ several tokens
+
+def test_gemm_brute_force_tokens():
+    """Batched oracle: every token's row against the exact rational matvec,
+    within fp64 summation error plus one fp32 rounding; tokens are
+    independent (a token's output does not depend on the others)."""
+    N, K, M = 3, 512, 4
+    q, d, _ = synth.problem(41, N, K)
+    g = synth.rng(42)
+    X = np.stack([synth.activations(g, K) for _ in range(M)])
+    codes, scales, bad = oracle.pack(_ternary_W(q, d))
+    assert bad == 0
+    Y = oracle.gemm(codes, scales, N, K, synth.bits(X))
+    for m in range(M):
+        exact = brute.exact_gemv(q, synth.bits(d), synth.bits(X[m]))
+        l1 = brute.exact_l1(q, synth.bits(d), synth.bits(X[m]))
+        for n in range(N):
+            e64 = Fraction(K * 2.0 ** -52) * l1[n]
+            ulp32 = Fraction(float(np.spacing(np.float32(abs(float(exact[n])) + float(e64)))))
+            assert abs(Fraction(float(Y[m, n])) - exact[n]) <= ulp32 / 2 + e64 + Fraction(1, 2 ** 149)
+    perm = [2, 0, 3, 1]
+    assert np.array_equal(oracle.gemm(codes, scales, N, K, synth.bits(X[perm])), Y[perm])
