@@ -197,6 +197,7 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
     ("c1 q/o 4096x4096 fp16", 4096, 4096, "f16", 1001),
     ("c2 fused gate+up 2x16384x4096 fp16", 16384, 4096, "gate_up", 1003),
     ("c3 down 4096x16384 int8 (fused quantize)", 4096, 16384, "i8", 1004),
+    ("batched gate 16384x4096, 16 tokens per call (tq2_gemm)", 16384, 4096, "gemm16", 1005),
 ]
 ROTATION_BYTES = 1.1e9  # > the 256 MB Infinity Cache: every timed call streams from HBM
 
@@ -227,6 +228,8 @@ def time_configs(torch, tq2, synth, reps=5):
             mats.append((c, s))
             xs = x if xs is None else xs
         nbytes = nmat * (N * K * 66 // 256 + 4 * N) + 2 * K  # x read once
+        if kind == "gemm16":
+            nbytes = N * K * 66 // 256 + 16 * (2 * K + 4 * N)  # weights once, 16 x and 16 y
         ncopy = max(2, int(np.ceil(ROTATION_BYTES / nbytes)))
         copies = [[(c.clone(), s.clone()) for (c, s) in mats] for _ in range(ncopy)]
         del mats
@@ -238,6 +241,12 @@ def time_configs(torch, tq2, synth, reps=5):
         elif kind == "gate_up":
             calls = [lambda j=j: tq2.tq2_gemv_gate_up(copies[j][0][0], copies[j][0][1], copies[j][1][0],
                                                       copies[j][1][1], xs, y=y.view(2, N)) for j in range(ncall)]
+        elif kind == "gemm16":
+            X16 = torch.stack([synth.torch_activations(seed + 1 + m, K) for m in range(16)])
+            Y16 = torch.empty(16, N, dtype=torch.float32, device="cuda")
+            ws16 = torch.empty(tq2.tq2_gemm_workspace_bytes(N, K, 16), dtype=torch.uint8, device="cuda")
+            calls = [lambda j=j: tq2.tq2_gemm(copies[j][0][0], copies[j][0][1], X16, y=Y16, ws=ws16)
+                     for j in range(ncall)]
         else:
             calls = [lambda j=j: tq2.tq2_gemv_i8(copies[j][0][0], copies[j][0][1], xs, sc, y=y)
                      for j in range(ncall)]
@@ -258,6 +267,16 @@ def time_configs(torch, tq2, synth, reps=5):
         torch.cuda.empty_cache()
         gbs = nbytes / us / 1e3
         rd_gbs = rb / us_rd / 1e3
+        if kind == "gemm16":
+            nbytes_tok = nbytes
+            gbs = nbytes / us / 1e3
+            out[label] = {"us_per_call": round(us, 3), "tokens_per_s": round(16e6 / us, 1),
+                          "weight_GB_s": round(gbs, 1), "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+                          "read_probe_us": round(us_rd, 3),
+                          "speedup_vs_16_gemv": None, "bytes_per_call": int(nbytes_tok),
+                          "rotation_copies": ncopy}
+            log(f"{label}: {us:.2f} us/call, {16e6 / us:.0f} tokens/s, weights at {gbs:.1f} GB/s")
+            continue
         out[label] = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1),
                       "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
                       "read_probe_us": round(us_rd, 3), "read_probe_GB_s": round(rd_gbs, 1),
@@ -337,6 +356,9 @@ def main():
     configs = None
     if not args.no_configs:
         configs = time_configs(torch, tq2, synth)
+        for label, rec in configs.items():
+            if "speedup_vs_16_gemv" in rec:  # same shape as the gate/up launches timed above
+                rec["speedup_vs_16_gemv"] = round(16 * us_dom / rec["us_per_call"], 2)
 
     cpu, parity = None, None
     if not args.no_cpu:
