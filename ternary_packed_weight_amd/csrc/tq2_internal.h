@@ -52,7 +52,7 @@ hipError_t launch_gemv_i8_requant(const MatSet& m, int64_t K, const uint16_t* x,
 // workspace holds the prepared activations and, when K is split across
 // workgroups, the split partials; plan_gemm fixes the tiling.
 struct GemmPlan {
-  int U, T, S;                // row groups per wave, steps per load batch, waves per workgroup
+  int U, T, S;                // row groups per wave, steps per load batch, chunk-waves per workgroup
   int64_t mt;                 // 16-token tiles
   int64_t splits, steps_per_split, wgs;
   int64_t xb_bytes, zt_bytes, part_bytes;

@@ -724,22 +724,25 @@ struct GemmArgs {
   const float* zt;
   float* out;         // y[M][N], or the split partials [splits][M][N]
   int64_t N, K, M;
-  int32_t steps_per_split;
+  int32_t steps_per_split;  // multiple of C*T
 };
 
-// Wave: U row groups x one K-split x one token tile.  Workgroup: S waves
-// (S row sets of the same split and tile).
-template <int U, int T>
-__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
+// Workgroup: C waves, the C chunks of one K-split of one row set (U row
+// groups) and one token tile; their sums meet in LDS and are added in chunk
+// order.  Grid: (row sets, K-splits, token tiles).
+template <int U, int T, int C>
+__global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
+  __shared__ float red[C][U][4][64];
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4, i = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int S = blockDim.x >> 6;
-  const int rset = (int)blockIdx.x * S + wave;
+  const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rset = blockIdx.x;
   const int split = blockIdx.y, tt = blockIdx.z;
   const int64_t row_bytes = a.K / 4, BK = a.K / kBlock, nseg = a.K / 64;
-  const int s_begin = split * a.steps_per_split;
-  const int s_end = (int)((int64_t)s_begin + a.steps_per_split < BK ? s_begin + a.steps_per_split : BK);
+  const int spw = a.steps_per_split / C;  // steps per wave
+  const int s_begin = split * a.steps_per_split + c * spw;
+  const int s_lim = s_begin + spw;
+  const int s_end = (int64_t)s_lim < BK ? s_lim : (int)BK;
 
   // per row group: scalar descriptors over its valid rows (zeros past N)
   __amdgpu_buffer_rsrc_t rc[U], rs[U];
@@ -763,12 +766,12 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
   for (int s0 = s_begin; s0 < s_end; s0 += T) {
     // issue, in this order (loads complete in issue order): the B operands
     // and zero points of up to T steps (L2), then the code words (HBM), then
-    // the scales.  Steps past the split read zeros.
+    // the scales.  Steps past the range read zeros (or are not used).
     uint4 bo[T][8];
     float z[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const int s = s0 + t < s_end ? s0 + t : s_begin;  // in range; unused when past the split
+      const int s = s0 + t < s_end ? s0 + t : s0;  // in range
       const uint4* bp = a.xb + ((int64_t)tt * nseg + 4 * s + G) * 8 * kTok + i;
 #pragma unroll
       for (int o = 0; o < 8; ++o) bo[t][o] = bp[o * kTok];
@@ -829,6 +832,23 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
     }
   }
 
+  // chunk sums meet in LDS; wave 0 adds them in chunk order and stores
+  if (C > 1) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[c][u][r][lane] = acc[u][r];
+    __syncthreads();
+    if (c != 0) return;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float sum = red[0][u][r][lane];
+        for (int cc = 1; cc < C; ++cc) sum += red[cc][u][r][lane];
+        acc[u][r] = sum;
+      }
+  }
   // lane (G, i): rows 4G..4G+3 of each group, token tt*16 + i
   const int64_t tok = (int64_t)tt * kTok + i;
   if (tok >= a.M) return;
@@ -856,20 +876,35 @@ GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
   GemmPlan p;
   p.U = 4;
   p.T = 2;
-  p.S = 4;
   p.mt = (M + kTok - 1) / kTok;
   const int64_t steps = K / kBlock;
   const int64_t rsets = ((N + kTileRows16 - 1) / kTileRows16 + p.U - 1) / p.U;
-  const int64_t wgs = (rsets + p.S - 1) / p.S;
-  const int64_t want = 2LL * device_cus();  // workgroups
-  int64_t splits = (want + wgs * p.mt - 1) / (wgs * p.mt);
-  if (splits < 1) splits = 1;
-  if (splits > steps) splits = steps;
-  int64_t sps = (steps + splits - 1) / splits;
-  sps = (sps + p.T - 1) / p.T * p.T;
+  // Pick C chunk-waves per workgroup (4 or 8: a 16-wave workgroup would cap
+  // the wave at 128 VGPRs, fewer than the kernel holds) and the number of K-splits
+  // across workgroups for about 8 waves per CU, preferring no split (split
+  // partials cost an extra pass) and then the fewest waves above the target.
+  const int64_t target = 8LL * device_cus();
+  int bestC = 4;
+  int64_t best_splits = 1, best_score = -1;
+  for (int C = 4; C <= 8; C *= 2) {
+    const int64_t per_split = (int64_t)C * p.T;
+    const int64_t max_splits = steps / per_split;  // every wave gets T steps or more
+    if (max_splits < 1 && C > 4) continue;
+    for (int64_t sp = 1; sp <= (max_splits > 1 ? max_splits : 1); sp *= 2) {
+      const int64_t waves = rsets * p.mt * sp * C;
+      // score: reaching the target matters most, then fewer splits, then fewer waves
+      const int64_t reach = waves >= target ? 1 : 0;
+      const int64_t score = reach * (1LL << 40) + (reach ? (64 - sp) * (1LL << 24) - waves : waves);
+      if (score > best_score) { best_score = score; bestC = C; best_splits = sp; }
+    }
+  }
+  p.S = bestC;
+  const int64_t per_split = (int64_t)bestC * p.T;
+  int64_t sps = (steps + best_splits - 1) / best_splits;
+  sps = (sps + per_split - 1) / per_split * per_split;
   p.splits = (steps + sps - 1) / sps;
   p.steps_per_split = sps;
-  p.wgs = wgs;
+  p.wgs = rsets;
   p.xb_bytes = p.mt * kTok * K * 2;
   p.zt_bytes = p.mt * kTok * steps * 4;
   p.part_bytes = p.splits > 1 ? p.splits * M * N * 4 : 0;
@@ -901,8 +936,11 @@ hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, 
   a.K = K;
   a.M = M;
   a.steps_per_split = (int32_t)p.steps_per_split;
-  hipLaunchKernelGGL((k_gemm_mfma<4, 2>), dim3((unsigned)p.wgs, (unsigned)p.splits, (unsigned)p.mt),
-                     dim3(64 * p.S), 0, st, a);
+  const dim3 grid((unsigned)p.wgs, (unsigned)p.splits, (unsigned)p.mt);
+  if (p.S == 8)
+    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 8>), grid, dim3(64 * 8), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 4>), grid, dim3(64 * 4), 0, st, a);
   if (p.splits > 1) {
     const int64_t MN = M * N;
     hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, part,
