@@ -204,10 +204,10 @@ int32_t tq2_gemv_i8_requant(const uint8_t *codes, const uint16_t *scales,
 /* ---- several tokens at once ---- */
 
 /* tq2_gemm_workspace_bytes -- device workspace that tq2_gemm needs for this
- * shape and token count: the activations prepared as matrix-core operands
- * (32*K bytes per started group of 16 tokens, plus K/4 bytes of block sums)
- * and, when the plan splits K across workgroups, the split partials
- * (4*M*N bytes per split).  (size_t)-1 for an invalid shape. */
+ * shape and token count: the split partials (4*M*N bytes per split) when the
+ * plan splits K across workgroups, which it does only when N gives too few
+ * row groups to fill the GPU; 0 otherwise.  (size_t)-1 for an invalid
+ * shape or token count. */
 size_t tq2_gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);
 
 /* tq2_gemm -- the matvec of page "BitCPM ternary (1.58-bit)" (kernel
@@ -216,11 +216,12 @@ size_t tq2_gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);
  * The weights are streamed once for all M tokens (prefill, speculative
  * decode; the page runs prefill as one matvec per token).  Per output the
  * accuracy of tq2_gemv: |Y - Y_ref| <= 2e-3 * sum_k |d_b(k) X[m][k]| + 1e-6.
- * 1 <= M <= TQ2_MAX_TOKENS.  ws: device memory of at least
- * tq2_gemm_workspace_bytes(N, K, M) bytes, 256-byte aligned, not
- * overlapping X or Y (TQ2_ERR_WORKSPACE otherwise); its contents on entry
- * do not matter and are overwritten.  Two to three kernels on `stream`;
- * deterministic (split partials are added in a fixed order). */
+ * 1 <= M <= TQ2_MAX_TOKENS.  ws: when tq2_gemm_workspace_bytes(N, K, M)
+ * is non-zero, device memory of at least that many bytes, 256-byte aligned,
+ * not overlapping X or Y (TQ2_ERR_WORKSPACE otherwise); its contents on
+ * entry do not matter and are overwritten.  Otherwise ws may be NULL.  One
+ * kernel on `stream` (two when K is split); deterministic (chunk and split
+ * sums are added in a fixed order). */
 #define TQ2_MAX_TOKENS 65536
 int32_t tq2_gemm(const uint8_t *codes, const uint16_t *scales, int64_t N,
                  int64_t K, const uint16_t *x, int64_t M, float *y, void *ws,

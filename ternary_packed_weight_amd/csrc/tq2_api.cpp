@@ -294,13 +294,13 @@ int32_t tq2_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_
   if (M * N > ((int64_t)1 << 40)) return TQ2_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, 4)) return TQ2_ERR_ALIGN;
   const size_t need = tq2::gemm_workspace_bytes(N, K, M);
-  if (!ws || ws_bytes < need || !aligned(ws, 256)) return TQ2_ERR_WORKSPACE;
+  if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return TQ2_ERR_WORKSPACE;
   const size_t xb = (size_t)(M * K) * 2, yb = (size_t)(M * N) * 4;
   const size_t cb = (size_t)(N * (K / 4)), sb = (size_t)(N * (K / TQ2_BLOCK)) * 2;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, codes, cb) || overlaps(y, yb, scales, sb))
     return TQ2_ERR_ARG;
-  if (overlaps(ws, need, x, xb) || overlaps(ws, need, y, yb) || overlaps(ws, need, codes, cb) ||
-      overlaps(ws, need, scales, sb))
+  if (need && (overlaps(ws, need, x, xb) || overlaps(ws, need, y, yb) || overlaps(ws, need, codes, cb) ||
+               overlaps(ws, need, scales, sb)))
     return TQ2_ERR_WORKSPACE;
   (void)hipGetLastError();
   return hip_status(tq2::launch_gemm(codes, scales, N, K, x, M, y, ws, (hipStream_t)stream));

@@ -49,13 +49,13 @@ hipError_t launch_gemv_i8_requant(const MatSet& m, int64_t K, const uint16_t* x,
                                   hipStream_t st);
 
 // Small-M batched matvec Y[M][N] = X[M][K] W^T (matrix cores).  The
-// workspace holds the prepared activations and, when K is split across
-// workgroups, the split partials; plan_gemm fixes the tiling.
+// workspace holds the split partials when K is split across workgroups
+// (otherwise nothing); plan_gemm fixes the tiling.
 struct GemmPlan {
   int U, T, S;                // row groups per wave, steps per load batch, chunk-waves per workgroup
   int64_t mt;                 // 16-token tiles
   int64_t splits, steps_per_split, wgs;
-  int64_t xb_bytes, zt_bytes, part_bytes;
+  int64_t part_bytes;
 };
 GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M);
 size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);

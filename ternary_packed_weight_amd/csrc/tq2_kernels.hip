@@ -655,12 +655,13 @@ hipError_t launch_gemv_silu_mul(const MatSet& m, int64_t K, const uint16_t* x, f
 // i = l%16) supplies row i's codes at k-slots 8G..8G+7 and token i's x
 // values at the same slots, and receives D[rows 4G..4G+3][token i].
 //
-//   prep   : X -> ready B operands (pairs scaled by 4^-j, the j-th mask
-//            position) and block zero points -sum(x)*2^-24, in the workspace;
-//   gemm   : a wave owns U row groups (16U rows) and a K-split; per 256-block
-//            step, 8 MFMAs per row group starting from the zero point, then
-//            acc += d_row * D;
-//   reduce : when K is split, the split partials are added in split order.
+//   gemm   : a wave owns U row groups (16U rows) and a K range; per 256-block
+//            step it builds the B operands of its token from X (pairs scaled
+//            by 4^-j, j the mask position, one byte permute each) and the
+//            block zero point -sum(x)*2^-24, then runs 8 MFMAs per row group
+//            starting from the zero point and does acc += d_row * D;
+//   reduce : when K is split across workgroups, the split partials are added
+//            in split order.
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -668,60 +669,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kTok = 16;        // tokens per tile (MFMA columns)
 constexpr int kTileRows16 = 16;  // rows per MFMA tile
 
-// Prep: one thread per (token of the padded tile set, 16-weight group).
-// xb[tt][K/64][8][16] uint4, operand 2j+h of segment s, token i, holding for
-// g = 0..3 the pair (x[64s+16g+4h+j], x[64s+16g+8+4h+j]) * 4^-j;
-// zt[tt][K/256][16] float.
-__global__ __launch_bounds__(256) void k_gemm_prep(const uint16_t* __restrict__ x, int64_t M,
-                                                   int64_t K, int64_t Mpad,
-                                                   uint4* __restrict__ xb, float* __restrict__ zt) {
-  const int64_t ng = K / 16;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool live = id < Mpad * ng;  // the grid is a multiple of 16 threads; see below
-  const int64_t tok = live ? id / ng : 0;
-  const int64_t g16 = live ? id - tok * ng : 0;
-  uint32_t xw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (live && tok < M) {
-    const uint4 a = *reinterpret_cast<const uint4*>(x + tok * K + 16 * g16);
-    const uint4 b = *reinterpret_cast<const uint4*>(x + tok * K + 16 * g16 + 8);
-    xw[0] = a.x; xw[1] = a.y; xw[2] = a.z; xw[3] = a.w;
-    xw[4] = b.x; xw[5] = b.y; xw[6] = b.z; xw[7] = b.w;
-  }
-  const int64_t tt = tok / kTok, ti = tok % kTok;
-  const int64_t seg = g16 >> 2, g = g16 & 3;
-  const int64_t nseg = K / 64;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e0 = 4 * h + j, e1 = 8 + 4 * h + j;  // x[16 g16 + e] is half e&1 of xw[e>>1]
-      const uint32_t sel = ((e0 & 1) ? 0x0302u : 0x0100u) | ((e1 & 1) ? 0x07060000u : 0x05040000u);
-      uint32_t pr = __builtin_amdgcn_perm(xw[e1 >> 1], xw[e0 >> 1], sel);
-      if (j) {
-        const half2v sc = {(_Float16)(1.0f / (float)(1 << (2 * j))), (_Float16)(1.0f / (float)(1 << (2 * j)))};
-        pr = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr) * sc);
-      }
-      if (live)
-        reinterpret_cast<uint32_t*>(xb + ((tt * nseg + seg) * 8 + (2 * j + h)) * kTok + ti)[g] = pr;
-    }
-  }
-  float s0 = dot2(xw[0], kOnesF16x2, 0.0f), s1 = dot2(xw[1], kOnesF16x2, 0.0f);
-  s0 = dot2(xw[2], kOnesF16x2, s0); s1 = dot2(xw[3], kOnesF16x2, s1);
-  s0 = dot2(xw[4], kOnesF16x2, s0); s1 = dot2(xw[5], kOnesF16x2, s1);
-  s0 = dot2(xw[6], kOnesF16x2, s0); s1 = dot2(xw[7], kOnesF16x2, s1);
-  float bs = s0 + s1;  // the 16 groups of one block are 16 consecutive threads (one DPP row)
-  bs += dpp_f32<0x128>(bs);
-  bs += dpp_f32<0x124>(bs);
-  bs += dpp_f32<0x122>(bs);
-  bs += dpp_f32<0x121>(bs);
-  if (live && (g16 & 15) == 0) zt[(tt * (K / kBlock) + (g16 >> 4)) * kTok + ti] = -ldexpf(bs, -24);
-}
-
 struct GemmArgs {
   const uint8_t* codes;
   const uint16_t* scales;
-  const uint4* xb;
-  const float* zt;
+  const uint16_t* x;  // X[M][K]
   float* out;         // y[M][N], or the split partials [splits][M][N]
   int64_t N, K, M;
   int32_t steps_per_split;  // multiple of C*T
@@ -738,7 +689,7 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
   const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rset = blockIdx.x;
   const int split = blockIdx.y, tt = blockIdx.z;
-  const int64_t row_bytes = a.K / 4, BK = a.K / kBlock, nseg = a.K / 64;
+  const int64_t row_bytes = a.K / 4, BK = a.K / kBlock;
   const int spw = a.steps_per_split / C;  // steps per wave
   const int s_begin = split * a.steps_per_split + c * spw;
   const int s_lim = s_begin + spw;
@@ -762,20 +713,22 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
   v4f acc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  int64_t tv = a.M - (int64_t)tt * kTok;
+  tv = tv > kTok ? kTok : tv;
+  const __amdgpu_buffer_rsrc_t xr = rsrc(a.x + (int64_t)tt * kTok * a.K, (uint32_t)(tv * a.K * 2));
 
   for (int s0 = s_begin; s0 < s_end; s0 += T) {
-    // issue, in this order (loads complete in issue order): the B operands
-    // and zero points of up to T steps (L2), then the code words (HBM), then
-    // the scales.  Steps past the range read zeros (or are not used).
-    uint4 bo[T][8];
-    float z[T];
+    // issue, in this order (loads complete in issue order): the x of up to
+    // T steps (64 values of this lane's token per step, L2), then the code
+    // words (HBM), then the scales.  Steps past the range read zeros (or are
+    // not used); tokens past M read zeros through the tile's descriptor.
+    uint4 xv[T][8];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int s = s0 + t < s_end ? s0 + t : s0;  // in range
-      const uint4* bp = a.xb + ((int64_t)tt * nseg + 4 * s + G) * 8 * kTok + i;
+      const int xoff = (int)((i * a.K + 256 * (int64_t)s + 64 * G) * 2);
 #pragma unroll
-      for (int o = 0; o < 8; ++o) bo[t][o] = bp[o * kTok];
-      z[t] = a.zt[((int64_t)tt * BK + s) * kTok + i];
+      for (int q = 0; q < 8; ++q) xv[t][q] = load_b128(xr, xoff + 16 * q);
     }
     uint4 w[T][U];
     uint16_t d[T][U][4];
@@ -808,13 +761,47 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (s0 + t >= s_end) break;  // uniform
+      uint32_t xw[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        xw[4 * q] = xv[t][q].x; xw[4 * q + 1] = xv[t][q].y; xw[4 * q + 2] = xv[t][q].z; xw[4 * q + 3] = xv[t][q].w;
+      }
+      uint4 bo[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t pr[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int e0 = 16 * g + 4 * h + j, e1 = e0 + 8;
+            const uint32_t sel = ((e0 & 1) ? 0x0302u : 0x0100u) | ((e1 & 1) ? 0x07060000u : 0x05040000u);
+            pr[g] = __builtin_amdgcn_perm(xw[e1 >> 1], xw[e0 >> 1], sel);
+            if (j) {
+              const half2v sc = {(_Float16)(1.0f / (float)(1 << (2 * j))), (_Float16)(1.0f / (float)(1 << (2 * j)))};
+              pr[g] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr[g]) * sc);
+            }
+          }
+          bo[2 * j + h] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+        }
+      }
+      float s0f = 0.0f, s1f = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        s0f = dot2(xw[2 * q], kOnesF16x2, s0f);
+        s1f = dot2(xw[2 * q + 1], kOnesF16x2, s1f);
+      }
+      float bsum = s0f + s1f;
+      bsum += __shfl_xor(bsum, 16, 64);
+      bsum += __shfl_xor(bsum, 32, 64);
+      const float zt_ = -ldexpf(bsum, -24);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t v[4] = {w[t][u].x, w[t][u].y, w[t][u].z, w[t][u].w};
         uint32_t v8[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) v8[g] = v[g] >> 8;
-        v4f D = v4f{z[t], z[t], z[t], z[t]};
+        v4f D = v4f{zt_, zt_, zt_, zt_};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t mask = 0x00030003u << (2 * j);
@@ -823,7 +810,7 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
             const uint32_t* src = h ? v8 : v;
             const uint4 av = make_uint4(src[0] & mask, src[1] & mask, src[2] & mask, src[3] & mask);
             D = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av),
-                                                       __builtin_bit_cast(v8h, bo[t][2 * j + h]), D, 0, 0, 0);
+                                                       __builtin_bit_cast(v8h, bo[2 * j + h]), D, 0, 0, 0);
           }
         }
 #pragma unroll
@@ -905,32 +892,23 @@ GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
   p.splits = (steps + sps - 1) / sps;
   p.steps_per_split = sps;
   p.wgs = rsets;
-  p.xb_bytes = p.mt * kTok * K * 2;
-  p.zt_bytes = p.mt * kTok * steps * 4;
   p.part_bytes = p.splits > 1 ? p.splits * M * N * 4 : 0;
   return p;
 }
 
 size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M) {
   const GemmPlan p = plan_gemm(N, K, M);
-  return (size_t)(p.xb_bytes + p.zt_bytes + p.part_bytes);
+  return (size_t)p.part_bytes;
 }
 
 hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                        const uint16_t* x, int64_t M, float* y, void* ws, hipStream_t st) {
   const GemmPlan p = plan_gemm(N, K, M);
-  uint8_t* wsb = static_cast<uint8_t*>(ws);
-  uint4* xb = reinterpret_cast<uint4*>(wsb);
-  float* zt = reinterpret_cast<float*>(wsb + p.xb_bytes);
-  float* part = reinterpret_cast<float*>(wsb + p.xb_bytes + p.zt_bytes);
-  const int64_t prep_threads = p.mt * kTok * (K / 16);
-  hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, x, M, K,
-                     p.mt * kTok, xb, zt);
+  float* part = static_cast<float*>(ws);
   GemmArgs a;
   a.codes = codes;
   a.scales = scales;
-  a.xb = xb;
-  a.zt = zt;
+  a.x = x;
   a.out = p.splits > 1 ? part : y;
   a.N = N;
   a.K = K;

@@ -303,9 +303,9 @@ def tq2_gemm(codes, scales, x, y=None, ws=None, stream=None):
     if y is None:
         y = torch.empty(M, N, dtype=torch.float32, device=codes.device)
     need = tq2_gemm_workspace_bytes(N, K, M)
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=codes.device)
-    wsb = ws.numel() * ws.element_size()
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=codes.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check("tq2_gemm", _lib.tq2_gemm(_ptr(codes), _ptr(scales), N, K, _ptr(x), M, _ptr(y), _ptr(ws), wsb,
                                       _stream(stream)))
     return y

@@ -181,3 +181,13 @@ def test_error_paths_gemm(tq2):
     assert g(w=0) == 4 and g(wb=need - 1) == 4 and g(w=ws + 16) == 4
     assert g(yy=x) == 1                      # y overlapping x
     assert g(w=y) == 4                       # workspace overlapping y
+
+
+@no_gpu
+def test_gemm_workspace_only_for_split_k(tq2):
+    """The 16384-row shapes run without a K split (no workspace); small N
+    splits K and needs the partials."""
+    lib = tq2.lib()
+    assert lib.tq2_gemm_workspace_bytes(16384, 4096, 16) == 0
+    assert lib.tq2_gemm_workspace_bytes(256, 4096, 16) % (4 * 16 * 256) == 0
+    assert lib.tq2_gemm_workspace_bytes(256, 4096, 16) > 0
