@@ -862,32 +862,25 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float* __restrict__ p
 GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
   GemmPlan p;
   p.U = 4;
-  p.T = 2;
   p.mt = (M + kTok - 1) / kTok;
   const int64_t steps = K / kBlock;
   const int64_t rsets = ((N + kTileRows16 - 1) / kTileRows16 + p.U - 1) / p.U;
-  // Pick C chunk-waves per workgroup (4 or 8: a 16-wave workgroup would cap
-  // the wave at 128 VGPRs, fewer than the kernel holds) and the number of K-splits
-  // across workgroups for about 8 waves per CU, preferring no split (split
-  // partials cost an extra pass) and then the fewest waves above the target.
+  // Measured on MI355X: when the row sets alone fill the CUs, or K is long
+  // (>= 8192), 8 chunk-waves per workgroup with 2 steps per load batch;
+  // otherwise (few rows, short K: K is split across workgroups anyway) 4
+  // chunk-waves with 1 step per batch, which keeps each wave's
+  // load-then-compute chain short.  Splits double until ~8 waves per CU or
+  // until every wave would get fewer than T steps.
+  const bool wide = rsets * p.mt >= device_cus() || steps >= 32;
+  p.T = wide ? 2 : 1;
+  p.S = (wide && steps >= 16) ? 8 : 4;
+  const int64_t per_split = (int64_t)p.S * p.T;
   const int64_t target = 8LL * device_cus();
-  int bestC = 4;
-  int64_t best_splits = 1, best_score = -1;
-  for (int C = 4; C <= 8; C *= 2) {
-    const int64_t per_split = (int64_t)C * p.T;
-    const int64_t max_splits = steps / per_split;  // every wave gets T steps or more
-    if (max_splits < 1 && C > 4) continue;
-    for (int64_t sp = 1; sp <= (max_splits > 1 ? max_splits : 1); sp *= 2) {
-      const int64_t waves = rsets * p.mt * sp * C;
-      // score: reaching the target matters most, then fewer splits, then fewer waves
-      const int64_t reach = waves >= target ? 1 : 0;
-      const int64_t score = reach * (1LL << 40) + (reach ? (64 - sp) * (1LL << 24) - waves : waves);
-      if (score > best_score) { best_score = score; bestC = C; best_splits = sp; }
-    }
-  }
-  p.S = bestC;
-  const int64_t per_split = (int64_t)bestC * p.T;
-  int64_t sps = (steps + best_splits - 1) / best_splits;
+  int64_t max_splits = steps / per_split;
+  if (max_splits < 1) max_splits = 1;
+  int64_t splits = 1;
+  while (splits * 2 <= max_splits && rsets * p.mt * splits * p.S < target) splits *= 2;
+  int64_t sps = (steps + splits - 1) / splits;
   sps = (sps + per_split - 1) / per_split * per_split;
   p.splits = (steps + sps - 1) / sps;
   p.steps_per_split = sps;
@@ -915,10 +908,12 @@ hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, 
   a.M = M;
   a.steps_per_split = (int32_t)p.steps_per_split;
   const dim3 grid((unsigned)p.wgs, (unsigned)p.splits, (unsigned)p.mt);
-  if (p.S == 8)
+  if (p.T == 2 && p.S == 8)
     hipLaunchKernelGGL((k_gemm_mfma<4, 2, 8>), grid, dim3(64 * 8), 0, st, a);
-  else
+  else if (p.T == 2)
     hipLaunchKernelGGL((k_gemm_mfma<4, 2, 4>), grid, dim3(64 * 4), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4>), grid, dim3(64 * 4), 0, st, a);
   if (p.splits > 1) {
     const int64_t MN = M * N;
     hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, part,
