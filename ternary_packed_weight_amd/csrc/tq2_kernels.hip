@@ -946,6 +946,24 @@ __device__ __forceinline__ int quantize_one(uint16_t xh, float s, float rs) {
   return (int)r;
 }
 
+// The same rule split for bulk use: the fast part gives rint(v) and whether
+// it can be trusted (near = too close to a half-integer, or v not finite);
+// the exact part is the IEEE division, taken for `near` values only.
+// With r = rint(v), t = v - r is exact and |t| <= 1/2; v is farther than
+// 8u|v| (u = 2^-24) from every half-integer exactly when |t| + |v| 2^-21 < 1/2.
+__device__ __forceinline__ float quantize_fast(uint16_t xh, float rs, bool& near) {
+  const float v = half_to_float(xh) * rs;
+  const float r = __builtin_rintf(v);
+  near = !(__builtin_fmaf(fabsf(v), 0x1p-21f, fabsf(v - r)) < 0.5f);  // NaN/inf land here too
+  return r;
+}
+
+__device__ __forceinline__ int quantize_exact(uint16_t xh, float s) {
+  float r = __builtin_rintf(half_to_float(xh) / s);
+  if (__builtin_isnan(r)) r = 0.0f;
+  return (int)fminf(fmaxf(r, -128.0f), 127.0f);
+}
+
 __global__ __launch_bounds__(256) void k_quantize_i8(const uint16_t* __restrict__ x, int64_t K,
                                                      float s, int8_t* __restrict__ xq) {
   const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1153,10 +1171,26 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
     int v[16];
     if (QUANT) {
       const uint32_t hw[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+      // fast path for all 16; the IEEE division only for values near a tie,
+      // behind a wave-uniform branch (almost never taken on real data: the
+      // compiler would otherwise evaluate the division for every value)
+      uint32_t near_mask = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[2 * i] = quantize_one((uint16_t)(hw[i] & 0xFFFFu), s, rs);
-        v[2 * i + 1] = quantize_one((uint16_t)(hw[i] >> 16), s, rs);
+      for (int e = 0; e < 16; ++e) {
+        bool nr;
+        const uint16_t h = (uint16_t)((e & 1) ? hw[e >> 1] >> 16 : hw[e >> 1] & 0xFFFFu);
+        const float r = quantize_fast(h, rs, nr);
+        v[e] = (int)fminf(fmaxf(r, -128.0f), 127.0f);  // NaN (near) -> -128, replaced below
+        near_mask |= (uint32_t)nr << e;
+      }
+      if (__builtin_amdgcn_ballot_w64(near_mask != 0)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if ((near_mask >> e) & 1u) {
+            const uint16_t h = (uint16_t)((e & 1) ? hw[e >> 1] >> 16 : hw[e >> 1] & 0xFFFFu);
+            v[e] = quantize_exact(h, s);
+          }
+        }
       }
     } else {
       const uint32_t bw[4] = {a4.x, a4.y, a4.z, a4.w};
