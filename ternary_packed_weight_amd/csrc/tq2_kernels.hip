@@ -656,12 +656,23 @@ hipError_t launch_gemv_silu_mul(const MatSet& m, int64_t K, const uint16_t* x, f
 // values at the same slots, and receives D[rows 4G..4G+3][token i].
 //
 //   gemm   : a wave owns U row groups (16U rows) and a K range; per 256-block
-//            step it builds the B operands of its token from X (pairs scaled
-//            by 4^-j, j the mask position, one byte permute each) and the
-//            block zero point -sum(x)*2^-24, then runs 8 MFMAs per row group
-//            starting from the zero point and does acc += d_row * D;
+//            step it builds the B operands of its token from X (one byte
+//            permute per pair, then a power-of-two scale, below) and the
+//            block zero point -sum(x) * 2^(-18-sh), then runs 8 MFMAs per row
+//            group starting from the zero point and does
+//            acc += d_row * 2^sh * D;
 //   reduce : when K is split across workgroups, the split partials are added
 //            in split order.
+//
+// Operand scale.  The mask at position j makes a code worth q * 4^j * 2^-24,
+// so the x paired with it is scaled by 4^(3-j) * 2^-sh, which makes every
+// product q * x * 2^(-18-sh).  For a (token, block) whose sum of x^2 is
+// below 2^16 (so every |x| < 256), sh = 0: the scale is up by 1..64, exact
+// in binary16 (no overflow below 16384, and scaling up never drops a bit).
+// Otherwise sh = 6 (scale 4^-j): x values tiny enough to be rounded lose at
+// most 2^-19 each, under 2^-10 |d| per block, against this block's share
+// 2e-3 |d| sum|x| >= 2e-3 |d| 256 of the tolerance.  (A plain 4^-j scale
+// for every block would round tiny activations, x near 2^-14, by up to 3%.)
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -766,9 +777,26 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
       for (int q = 0; q < 8; ++q) {
         xw[4 * q] = xv[t][q].x; xw[4 * q + 1] = xv[t][q].y; xw[4 * q + 2] = xv[t][q].z; xw[4 * q + 3] = xv[t][q].w;
       }
+      // block sums of x and x^2 (the four lanes of a token hold its block)
+      float s0f = 0.0f, s1f = 0.0f, q0f = 0.0f, q1f = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        s0f = dot2(xw[2 * q], kOnesF16x2, s0f);
+        s1f = dot2(xw[2 * q + 1], kOnesF16x2, s1f);
+        q0f = dot2(xw[2 * q], xw[2 * q], q0f);
+        q1f = dot2(xw[2 * q + 1], xw[2 * q + 1], q1f);
+      }
+      float bsum = s0f + s1f, bsq = q0f + q1f;
+      bsum += __shfl_xor(bsum, 16, 64);
+      bsq += __shfl_xor(bsq, 16, 64);
+      bsum += __shfl_xor(bsum, 32, 64);
+      bsq += __shfl_xor(bsq, 32, 64);
+      const int sh = bsq < 65536.0f ? 0 : 6;  // not finite: 6
       uint4 bo[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const uint32_t hb = (uint32_t)(21 - 2 * j - sh) << 10;  // binary16 2^(6-2j-sh)
+        const half2v sc = __builtin_bit_cast(half2v, hb | (hb << 16));
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           uint32_t pr[4];
@@ -777,24 +805,14 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
             const int e0 = 16 * g + 4 * h + j, e1 = e0 + 8;
             const uint32_t sel = ((e0 & 1) ? 0x0302u : 0x0100u) | ((e1 & 1) ? 0x07060000u : 0x05040000u);
             pr[g] = __builtin_amdgcn_perm(xw[e1 >> 1], xw[e0 >> 1], sel);
-            if (j) {
-              const half2v sc = {(_Float16)(1.0f / (float)(1 << (2 * j))), (_Float16)(1.0f / (float)(1 << (2 * j)))};
-              pr[g] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr[g]) * sc);
-            }
+            pr[g] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr[g]) * sc);
           }
           bo[2 * j + h] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
         }
       }
-      float s0f = 0.0f, s1f = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        s0f = dot2(xw[2 * q], kOnesF16x2, s0f);
-        s1f = dot2(xw[2 * q + 1], kOnesF16x2, s1f);
-      }
-      float bsum = s0f + s1f;
-      bsum += __shfl_xor(bsum, 16, 64);
-      bsum += __shfl_xor(bsum, 32, 64);
-      const float zt_ = -ldexpf(bsum, -24);
+      const float zt_ = -ldexpf(bsum, -18 - sh);
+      const bool any_sh = __builtin_amdgcn_ballot_w64(sh != 0) != 0;  // wave-uniform
+      const float fsh = sh ? 64.0f : 1.0f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t v[4] = {w[t][u].x, w[t][u].y, w[t][u].z, w[t][u].w};
@@ -813,6 +831,7 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
                                                        __builtin_bit_cast(v8h, bo[2 * j + h]), D, 0, 0, 0);
           }
         }
+        if (any_sh) D *= fsh;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[u][r] = __builtin_fmaf(half_to_float(d[t][u][r]), D[r], acc[u][r]);
       }
@@ -845,7 +864,7 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
     const int64_t gi = (int64_t)rset * U + u;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * G + r < valid[u]) o[gi * kTileRows16 + 4 * G + r] = ldexpf(acc[u][r], 24);
+      if (4 * G + r < valid[u]) o[gi * kTileRows16 + 4 * G + r] = ldexpf(acc[u][r], 18);
   }
 }
 

@@ -151,6 +151,38 @@ def test_gemv_f16_one_hot_exact(tq2):
         assert np.array_equal(ys[k].cpu().numpy(), expect), k
 
 
+def _range_activations(kind, K, g):
+    """Activations that stress how the fp16 paths scale x before the products:
+    a constant tiny value (2^-14 + 2^-19 - 2^-24) whose low bits a 4^-3
+    down-scale would round away, every one in the same direction; tiny
+    random values; blocks holding values >= 256; values near the binary16
+    maximum."""
+    if kind == "const_tiny":
+        return np.full(K, 2.0**-14 + 2.0**-19 - 2.0**-24, np.float16)
+    if kind == "tiny":
+        return (g.standard_normal(K) * 2.0**-12).astype(np.float16)
+    if kind == "big_blocks":
+        x = synth.activations(g, K).copy()
+        x[g.integers(0, K, 8)] = np.float16(3000.0)
+        return x
+    assert kind == "near_max"
+    return (g.uniform(-1.0, 1.0, K) * 60000.0).astype(np.float16)
+
+
+RANGE_KINDS = ["const_tiny", "tiny", "big_blocks", "near_max"]
+
+
+@pytest.mark.parametrize("kind", RANGE_KINDS)
+def test_gemv_f16_activation_ranges(tq2, kind):
+    N, K = 300, 4352
+    _, c, s, _ = _packed(2100, N, K)
+    x = _range_activations(kind, K, synth.rng(2101))
+    dc, ds, xd = _to_dev(c, s, x)
+    y = tq2.tq2_gemv(dc, ds, xd)
+    torch.cuda.synchronize()
+    _check_f16(y.cpu().numpy(), oracle.gemv(c, s, N, K, synth.bits(x)), _tol(s, x, N, K))
+
+
 def test_gemv_f16_special_values(tq2):
     N, K = 8, 1024
     q, codes, scales, x = _packed(510, N, K)
@@ -462,3 +494,20 @@ def test_gemm_token_independence_and_determinism(tq2):
     assert torch.equal(Y1, Y2)
     assert torch.equal(Y1[5], Y3[0])
     _check_f16(Y1[5].cpu().numpy(), Yv.cpu().numpy().astype(np.float64), 2 * _tol(s, X[5], N, K))
+
+
+@pytest.mark.parametrize("kind", RANGE_KINDS)
+def test_gemm_activation_ranges(tq2, kind):
+    """The batched path scales its B operands per (token, block); tiny
+    activations must come through exactly and large ones within tolerance."""
+    N, K, M = 300, 4352, 3
+    _, c, s, _ = _packed(2200, N, K)
+    g = synth.rng(2201)
+    X = np.stack([_range_activations(kind, K, g) for _ in range(M)])
+    dc, ds = _to_dev(c, s)
+    Y = tq2.tq2_gemm(dc, ds, torch.from_numpy(np.ascontiguousarray(X, np.float16)).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.gemm(c, s, N, K, synth.bits(X))
+    Yc = Y.cpu().numpy()
+    for m in range(M):
+        _check_f16(Yc[m], ref[m], _tol(s, X[m], N, K))
