@@ -965,16 +965,25 @@ __device__ __forceinline__ int quantize_one(uint16_t xh, float s, float rs) {
   return (int)r;
 }
 
-// The same rule split for bulk use: the fast part gives rint(v) and whether
+// The same rule split for bulk use: the fast part gives the code and whether
 // it can be trusted (near = too close to a half-integer, or v not finite);
 // the exact part is the IEEE division, taken for `near` values only.
-// With r = rint(v), t = v - r is exact and |t| <= 1/2; v is farther than
-// 8u|v| (u = 2^-24) from every half-integer exactly when |t| + |v| 2^-21 < 1/2.
-__device__ __forceinline__ float quantize_fast(uint16_t xh, float rs, bool& near) {
-  const float v = half_to_float(xh) * rs;
-  const float r = __builtin_rintf(v);
-  near = !(__builtin_fmaf(fabsf(v), 0x1p-21f, fabsf(v - r)) < 0.5f);  // NaN/inf land here too
-  return r;
+// v = RN(x * rs) is clamped first, c = clamp(v) in [-128, 127]: beyond 127
+// (below -128) both sides of a tie clamp to the same code, so clamped values
+// never need the division.  c + 1.5*2^23 rounds c to an integer (ties to
+// even) in the low mantissa bits, so the low byte of that float is x_q (two's
+// complement), and subtracting 1.5*2^23 again gives r = rint(c) exactly.
+// t = c - r is exact with |t| <= 1/2, and c (when not clamped) is farther
+// than 8u|c| (u = 2^-24) from every half-integer exactly when
+// |t| + |c| 2^-21 < 1/2.  The test uses |v| for the margin, so NaN, the
+// infinities and |v| >= 2^20 also land on the exact path.
+__device__ __forceinline__ uint32_t quantize_fast_bits(uint16_t xh, float rs, bool& near) {
+  const float v = __builtin_fmaf(half_to_float(xh), rs, 0.0f);  // RN(x * rs)
+  const float c = __builtin_amdgcn_fmed3f(v, -128.0f, 127.0f);
+  const float m = c + 0x1.8p23f;
+  const float t = c - (m - 0x1.8p23f);
+  near = !(__builtin_fmaf(fabsf(v), 0x1p-21f, fabsf(t)) < 0.5f);
+  return __builtin_bit_cast(uint32_t, m);
 }
 
 __device__ __forceinline__ int quantize_exact(uint16_t xh, float s) {
@@ -1130,7 +1139,7 @@ template <int R, bool QUANT, bool PARTIALS, int CT, int MAXT, bool REQUANT = fal
 __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
                                                   const uint16_t* __restrict__ x,
                                                   const int8_t* __restrict__ xq_in, float s,
-                                                  float* __restrict__ y,
+                                                  float rs, float* __restrict__ y,
                                                   int32_t* __restrict__ partials, Split sp,
                                                   Requant rq) {
   extern __shared__ uint4 lds[];
@@ -1181,46 +1190,49 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
   //     (m / 4) % 64 of chunk m / 256.  Every thread quantizes and stores;
   //     one without a group stores into the sink (no branch for the x
   //     loads to sink into).
-  const float rs = 1.0f / s;
 #pragma unroll
   for (int p = 0; p < XP; ++p) {
     const int m = tid + p * (int)blockDim.x;
     const bool staged = m < ngroups;
     const uint4 a4 = xa[p], b4 = xb[p];
-    int v[16];
+    // mb[e]: a float whose low byte is x_q of element e
+    uint32_t mb[16];
     if (QUANT) {
       const uint32_t hw[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
       // fast path for all 16; the IEEE division only for values near a tie,
       // behind a wave-uniform branch (almost never taken on real data: the
       // compiler would otherwise evaluate the division for every value)
-      uint32_t near_mask = 0;
+      bool any_near = false;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        bool nr;
         const uint16_t h = (uint16_t)((e & 1) ? hw[e >> 1] >> 16 : hw[e >> 1] & 0xFFFFu);
-        const float r = quantize_fast(h, rs, nr);
-        v[e] = (int)fminf(fmaxf(r, -128.0f), 127.0f);  // NaN (near) -> -128, replaced below
-        near_mask |= (uint32_t)nr << e;
+        bool nr;
+        mb[e] = quantize_fast_bits(h, rs, nr);
+        any_near |= nr;
       }
-      if (__builtin_amdgcn_ballot_w64(near_mask != 0)) {
+      if (__builtin_amdgcn_ballot_w64(any_near)) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          if ((near_mask >> e) & 1u) {
-            const uint16_t h = (uint16_t)((e & 1) ? hw[e >> 1] >> 16 : hw[e >> 1] & 0xFFFFu);
-            v[e] = quantize_exact(h, s);
-          }
+          const uint16_t h = (uint16_t)((e & 1) ? hw[e >> 1] >> 16 : hw[e >> 1] & 0xFFFFu);
+          bool nr;
+          (void)quantize_fast_bits(h, rs, nr);
+          if (nr) mb[e] = (uint32_t)quantize_exact(h, s) & 0xFFu;
         }
       }
     } else {
       const uint32_t bw[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = (int)(int8_t)((bw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+      for (int i = 0; i < 16; ++i) mb[i] = bw[i >> 2] >> (8 * (i & 3));
     }
+    // dword j holds x_q of elements j, 4+j, 8+j, 12+j (low bytes, one permute
+    // per pair and one for the halves)
     uint32_t dw[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dw[j] = ((uint32_t)v[j] & 0xFFu) | (((uint32_t)v[4 + j] & 0xFFu) << 8) |
-              (((uint32_t)v[8 + j] & 0xFFu) << 16) | (((uint32_t)v[12 + j] & 0xFFu) << 24);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = __builtin_amdgcn_perm(mb[4 + j], mb[j], 0x0C0C0400u);
+      const uint32_t hi = __builtin_amdgcn_perm(mb[12 + j], mb[8 + j], 0x04000C0Cu);
+      dw[j] = lo | hi;
+    }
     const int ch = m >> 8, ln = (m >> 2) & 63, gg = m & 3;
     *(staged ? xs + (ch * 4 + gg) * 64 + ln : sink) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
   }
@@ -1292,19 +1304,19 @@ static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, con
   const int ct = sp.C <= 4 && sp.C != 3 ? sp.C : 0;
   if ((int64_t)f16_stage_passes(ct) * b.x < K / 16) return hipErrorInvalidConfiguration;
   if (sp.C == 1)
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 1, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, y,
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 1, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, 1.0f / s, y,
                        partials, sp, rq);
   else if (sp.C == 2)
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 2, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, y,
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 2, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, 1.0f / s, y,
                        partials, sp, rq);
   else if (sp.C == 4)
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 4, 1024, REQUANT>), g, b, lds, st, m, K, x, xq, s,
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 4, 1024, REQUANT>), g, b, lds, st, m, K, x, xq, s, 1.0f / s,
                        y, partials, sp, rq);
   else if (b.x <= 512)
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, y,
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 512, REQUANT>), g, b, lds, st, m, K, x, xq, s, 1.0f / s, y,
                        partials, sp, rq);
   else
-    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 1024, REQUANT>), g, b, lds, st, m, K, x, xq, s,
+    hipLaunchKernelGGL((k_gemv_i8<R, QUANT, PARTIALS, 0, 1024, REQUANT>), g, b, lds, st, m, K, x, xq, s, 1.0f / s,
                        y, partials, sp, rq);
   return hipGetLastError();
 }

@@ -298,13 +298,16 @@ def test_quantize_ties_and_clamps(tq2):
 
 def test_gemv_i8_fused_quantizer_all_fp16(tq2):
     """The quantizer inside the fused int8 matvec agrees with the oracle on
-    every finite binary16 activation (K = 65280 covers 63488 of them)."""
+    every finite binary16 activation (K = 65280 covers 63488 of them), for
+    scales with many exact ties (powers of two, 1/127), ordinary ones, one so
+    small that most values clamp and one so large that most round to 0."""
     allh = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
     allh = allh[np.isfinite(allh)][:65280].astype(np.float16)
     K = allh.size
-    N = 3
+    N = 8
     q, codes, scales, _ = _packed(970, N, K)
-    for s in (np.float32(0.5), np.float32(1.0 / 3.0), np.float32(0.0371)):
+    for s in (np.float32(0.5), np.float32(0.25), np.float32(1.0 / 3.0), np.float32(0.0371),
+              np.float32(0.1), np.float32(1.0 / 127.0), np.float32(2.0**-9), np.float32(1000.0)):
         c, sc, xd = _to_dev(codes, scales, allh)
         P = torch.empty((N, K // 256), dtype=torch.int32, device=DEV)
         y = tq2.tq2_gemv_i8(c, sc, xd, s)
