@@ -690,16 +690,18 @@ struct GemmArgs {
 };
 
 // Workgroup: C waves, the C chunks of one K-split of one row set (U row
-// groups) and one token tile; their sums meet in LDS and are added in chunk
-// order.  Grid: (row sets, K-splits, token tiles).
-template <int U, int T, int C>
+// groups) and TT token tiles; their sums meet in LDS and are added in chunk
+// order.  A wave decodes each code word once for all TT tiles (the A
+// operand is shared; each tile brings its own B operands).  Grid: (row sets,
+// K-splits, token tiles / TT).
+template <int U, int T, int C, int TT>
 __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
-  __shared__ float red[C][U][4][64];
+  __shared__ float red[C][TT][U][4][64];
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4, i = lane & 15;
   const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rset = blockIdx.x;
-  const int split = blockIdx.y, tt = blockIdx.z;
+  const int split = blockIdx.y, tt0 = blockIdx.z * TT;
   const int64_t row_bytes = a.K / 4, BK = a.K / kBlock;
   const int spw = a.steps_per_split / C;  // steps per wave
   const int s_begin = split * a.steps_per_split + c * spw;
@@ -721,25 +723,36 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
     rs[u] = rsrc(a.scales + r0 * BK, (uint32_t)(v * BK * 2));
   }
 
-  v4f acc[U];
+  v4f acc[TT][U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  int64_t tv = a.M - (int64_t)tt * kTok;
-  tv = tv > kTok ? kTok : tv;
-  const __amdgpu_buffer_rsrc_t xr = rsrc(a.x + (int64_t)tt * kTok * a.K, (uint32_t)(tv * a.K * 2));
+  for (int q = 0; q < TT; ++q)
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[q][u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  // token tiles past M (the last of a pair) read zeros and store nothing
+  __amdgpu_buffer_rsrc_t xr[TT];
+#pragma unroll
+  for (int q = 0; q < TT; ++q) {
+    int64_t tv = a.M - (int64_t)(tt0 + q) * kTok;
+    tv = tv > kTok ? kTok : (tv < 0 ? 0 : tv);
+    const int64_t base = tv > 0 ? (int64_t)(tt0 + q) * kTok * a.K : 0;
+    xr[q] = rsrc(a.x + base, (uint32_t)(tv * a.K * 2));
+  }
 
   for (int s0 = s_begin; s0 < s_end; s0 += T) {
     // issue, in this order (loads complete in issue order): the x of up to
-    // T steps (64 values of this lane's token per step, L2), then the code
-    // words (HBM), then the scales.  Steps past the range read zeros (or are
-    // not used); tokens past M read zeros through the tile's descriptor.
-    uint4 xv[T][8];
+    // T steps for each tile (64 values of this lane's token per step, L2),
+    // then the code words (HBM), then the scales.  Steps past the range
+    // read zeros (or are not used); tokens past M read zeros through their
+    // tile's descriptor.
+    uint4 xv[TT][T][8];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int s = s0 + t < s_end ? s0 + t : s0;  // in range
       const int xoff = (int)((i * a.K + 256 * (int64_t)s + 64 * G) * 2);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) xv[t][q] = load_b128(xr, xoff + 16 * q);
+      for (int q = 0; q < TT; ++q)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xv[q][t][k] = load_b128(xr[q], xoff + 16 * k);
     }
     uint4 w[T][U];
     uint16_t d[T][U][4];
@@ -772,54 +785,62 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (s0 + t >= s_end) break;  // uniform
-      uint32_t xw[32];
+      uint4 bo[TT][8];
+      float zt[TT], fsh[TT];
+      bool any_sh[TT];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        xw[4 * q] = xv[t][q].x; xw[4 * q + 1] = xv[t][q].y; xw[4 * q + 2] = xv[t][q].z; xw[4 * q + 3] = xv[t][q].w;
-      }
-      // block sums of x and x^2 (the four lanes of a token hold its block)
-      float s0f = 0.0f, s1f = 0.0f, q0f = 0.0f, q1f = 0.0f;
+      for (int q = 0; q < TT; ++q) {
+        uint32_t xw[32];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        s0f = dot2(xw[2 * q], kOnesF16x2, s0f);
-        s1f = dot2(xw[2 * q + 1], kOnesF16x2, s1f);
-        q0f = dot2(xw[2 * q], xw[2 * q], q0f);
-        q1f = dot2(xw[2 * q + 1], xw[2 * q + 1], q1f);
-      }
-      float bsum = s0f + s1f, bsq = q0f + q1f;
-      bsum += __shfl_xor(bsum, 16, 64);
-      bsq += __shfl_xor(bsq, 16, 64);
-      bsum += __shfl_xor(bsum, 32, 64);
-      bsq += __shfl_xor(bsq, 32, 64);
-      const int sh = bsq < 65536.0f ? 0 : 6;  // not finite: 6
-      uint4 bo[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t hb = (uint32_t)(21 - 2 * j - sh) << 10;  // binary16 2^(6-2j-sh)
-        const half2v sc = __builtin_bit_cast(half2v, hb | (hb << 16));
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t pr[4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int e0 = 16 * g + 4 * h + j, e1 = e0 + 8;
-            const uint32_t sel = ((e0 & 1) ? 0x0302u : 0x0100u) | ((e1 & 1) ? 0x07060000u : 0x05040000u);
-            pr[g] = __builtin_amdgcn_perm(xw[e1 >> 1], xw[e0 >> 1], sel);
-            pr[g] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr[g]) * sc);
-          }
-          bo[2 * j + h] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+        for (int k = 0; k < 8; ++k) {
+          xw[4 * k] = xv[q][t][k].x; xw[4 * k + 1] = xv[q][t][k].y;
+          xw[4 * k + 2] = xv[q][t][k].z; xw[4 * k + 3] = xv[q][t][k].w;
         }
+        // block sums of x and x^2 (the four lanes of a token hold its block)
+        float s0f = 0.0f, s1f = 0.0f, q0f = 0.0f, q1f = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          s0f = dot2(xw[2 * k], kOnesF16x2, s0f);
+          s1f = dot2(xw[2 * k + 1], kOnesF16x2, s1f);
+          q0f = dot2(xw[2 * k], xw[2 * k], q0f);
+          q1f = dot2(xw[2 * k + 1], xw[2 * k + 1], q1f);
+        }
+        float bsum = s0f + s1f, bsq = q0f + q1f;
+        bsum += __shfl_xor(bsum, 16, 64);
+        bsq += __shfl_xor(bsq, 16, 64);
+        bsum += __shfl_xor(bsum, 32, 64);
+        bsq += __shfl_xor(bsq, 32, 64);
+        const int sh = bsq < 65536.0f ? 0 : 6;  // not finite: 6
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t hb = (uint32_t)(21 - 2 * j - sh) << 10;  // binary16 2^(6-2j-sh)
+          const half2v sc = __builtin_bit_cast(half2v, hb | (hb << 16));
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uint32_t pr[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int e0 = 16 * g + 4 * h + j, e1 = e0 + 8;
+              const uint32_t sel = ((e0 & 1) ? 0x0302u : 0x0100u) | ((e1 & 1) ? 0x07060000u : 0x05040000u);
+              pr[g] = __builtin_amdgcn_perm(xw[e1 >> 1], xw[e0 >> 1], sel);
+              pr[g] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr[g]) * sc);
+            }
+            bo[q][2 * j + h] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+          }
+        }
+        zt[q] = -ldexpf(bsum, -18 - sh);
+        any_sh[q] = __builtin_amdgcn_ballot_w64(sh != 0) != 0;  // wave-uniform
+        fsh[q] = sh ? 64.0f : 1.0f;
       }
-      const float zt_ = -ldexpf(bsum, -18 - sh);
-      const bool any_sh = __builtin_amdgcn_ballot_w64(sh != 0) != 0;  // wave-uniform
-      const float fsh = sh ? 64.0f : 1.0f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t v[4] = {w[t][u].x, w[t][u].y, w[t][u].z, w[t][u].w};
         uint32_t v8[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) v8[g] = v[g] >> 8;
-        v4f D = v4f{zt_, zt_, zt_, zt_};
+        v4f D[TT];
+#pragma unroll
+        for (int q = 0; q < TT; ++q) D[q] = v4f{zt[q], zt[q], zt[q], zt[q]};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t mask = 0x00030003u << (2 * j);
@@ -827,13 +848,20 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
           for (int h = 0; h < 2; ++h) {
             const uint32_t* src = h ? v8 : v;
             const uint4 av = make_uint4(src[0] & mask, src[1] & mask, src[2] & mask, src[3] & mask);
-            D = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av),
-                                                       __builtin_bit_cast(v8h, bo[2 * j + h]), D, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < TT; ++q)
+              D[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av),
+                                                            __builtin_bit_cast(v8h, bo[q][2 * j + h]),
+                                                            D[q], 0, 0, 0);
           }
         }
-        if (any_sh) D *= fsh;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[u][r] = __builtin_fmaf(half_to_float(d[t][u][r]), D[r], acc[u][r]);
+        for (int q = 0; q < TT; ++q) {
+          if (any_sh[q]) D[q] *= fsh[q];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[q][u][r] = __builtin_fmaf(half_to_float(d[t][u][r]), D[q][r], acc[q][u][r]);
+        }
       }
     }
   }
@@ -841,30 +869,37 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
   // chunk sums meet in LDS; wave 0 adds them in chunk order and stores
   if (C > 1) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int q = 0; q < TT; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[c][u][r][lane] = acc[u][r];
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[c][q][u][r][lane] = acc[q][u][r];
     __syncthreads();
     if (c != 0) return;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int q = 0; q < TT; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float sum = red[0][u][r][lane];
-        for (int cc = 1; cc < C; ++cc) sum += red[cc][u][r][lane];
-        acc[u][r] = sum;
-      }
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float sum = red[0][q][u][r][lane];
+          for (int cc = 1; cc < C; ++cc) sum += red[cc][q][u][r][lane];
+          acc[q][u][r] = sum;
+        }
   }
-  // lane (G, i): rows 4G..4G+3 of each group, token tt*16 + i
-  const int64_t tok = (int64_t)tt * kTok + i;
-  if (tok >= a.M) return;
-  float* o = a.out + ((int64_t)split * a.M + tok) * a.N;
+  // lane (G, i): rows 4G..4G+3 of each group, token (tt0 + q)*16 + i
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t gi = (int64_t)rset * U + u;
+  for (int q = 0; q < TT; ++q) {
+    const int64_t tok = (int64_t)(tt0 + q) * kTok + i;
+    if (tok >= a.M) continue;
+    float* o = a.out + ((int64_t)split * a.M + tok) * a.N;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (4 * G + r < valid[u]) o[gi * kTileRows16 + 4 * G + r] = ldexpf(acc[u][r], 18);
+    for (int u = 0; u < U; ++u) {
+      const int64_t gi = (int64_t)rset * U + u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * G + r < valid[u]) o[gi * kTileRows16 + 4 * G + r] = ldexpf(acc[q][u][r], 18);
+    }
   }
 }
 
@@ -884,21 +919,29 @@ GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
   p.mt = (M + kTok - 1) / kTok;
   const int64_t steps = K / kBlock;
   const int64_t rsets = ((N + kTileRows16 - 1) / kTileRows16 + p.U - 1) / p.U;
+  // Two token tiles per wave (one decode of the weights for 32 tokens, one
+  // step per load batch to bound the registers) once there are two tiles and
+  // the matrix is large (>= 2^26 weights: the gate/up and down shapes).
+  // Measured on MI355X: 16384x4096 at 64 tokens 41 -> 28 us, 4096x16384 at
+  // 48 tokens 39 -> 29 us; smaller matrices lose more parallelism than they
+  // save (256x4096 at 32 tokens 7.2 -> 9.2 us), so they keep one tile.
+  p.TT = (p.mt >= 2 && rsets * steps >= 4096) ? 2 : 1;
+  p.zt = (p.mt + p.TT - 1) / p.TT;
   // Measured on MI355X: when the row sets alone fill the CUs, or K is long
   // (>= 8192), 8 chunk-waves per workgroup with 2 steps per load batch;
   // otherwise (few rows, short K: K is split across workgroups anyway) 4
   // chunk-waves with 1 step per batch, which keeps each wave's
   // load-then-compute chain short.  Splits double until ~8 waves per CU or
   // until every wave would get fewer than T steps.
-  const bool wide = rsets * p.mt >= device_cus() || steps >= 32;
-  p.T = wide ? 2 : 1;
-  p.S = (wide && steps >= 16) ? 8 : 4;
+  const bool wide = rsets * p.zt >= device_cus() || steps >= 32;
+  p.T = (wide && p.TT == 1) ? 2 : 1;
+  p.S = (wide && steps >= 16 && p.TT == 1) ? 8 : 4;  // two tiles: 4 waves (registers)
   const int64_t per_split = (int64_t)p.S * p.T;
   const int64_t target = 8LL * device_cus();
   int64_t max_splits = steps / per_split;
   if (max_splits < 1) max_splits = 1;
   int64_t splits = 1;
-  while (splits * 2 <= max_splits && rsets * p.mt * splits * p.S < target) splits *= 2;
+  while (splits * 2 <= max_splits && rsets * p.zt * splits * p.S < target) splits *= 2;
   int64_t sps = (steps + splits - 1) / splits;
   sps = (sps + per_split - 1) / per_split * per_split;
   p.splits = (steps + sps - 1) / sps;
@@ -926,13 +969,15 @@ hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, 
   a.K = K;
   a.M = M;
   a.steps_per_split = (int32_t)p.steps_per_split;
-  const dim3 grid((unsigned)p.wgs, (unsigned)p.splits, (unsigned)p.mt);
-  if (p.T == 2 && p.S == 8)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 8>), grid, dim3(64 * 8), 0, st, a);
+  const dim3 grid((unsigned)p.wgs, (unsigned)p.splits, (unsigned)p.zt);
+  if (p.TT == 2)
+    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 2>), grid, dim3(64 * 4), 0, st, a);
+  else if (p.T == 2 && p.S == 8)
+    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 8, 1>), grid, dim3(64 * 8), 0, st, a);
   else if (p.T == 2)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 4>), grid, dim3(64 * 4), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 4, 1>), grid, dim3(64 * 4), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4>), grid, dim3(64 * 4), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 1>), grid, dim3(64 * 4), 0, st, a);
   if (p.splits > 1) {
     const int64_t MN = M * N;
     hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, part,
