@@ -164,10 +164,24 @@ def cpu_leg(host_layer0, ys_layer0, min_seconds):
         err = np.abs(yg.astype(np.float64) - yr.astype(np.float64))
         worst = max(worst, float((err / tol).max()))
         ok = ok and bool(np.all(err <= tol))
+    cores = oracle.threads()
+    # the same work on one thread, on a shorter bounded sample
+    oracle.set_threads(1)
+    reps1, t1 = 0, time.perf_counter()
+    while True:
+        for (e, c, s) in packed:
+            oracle.gemv(c, s, e["N"], e["K"], synth.bits(e["x"]))
+        reps1 += 1
+        if time.perf_counter() - t1 >= min_seconds / 3:
+            break
+    dt1 = time.perf_counter() - t1
+    oracle.set_threads(cores)
     cpu = {"value": round(layer_bytes * reps / dt / 1e9, 4), "unit": "GB/s",
-           "cores": oracle.threads(), "kind": "oracle",
+           "cores": cores, "kind": "oracle",
            "sample": f"decode layer 0 (7 linears, {sum(e['N'] * e['K'] for e in host_layer0)} weights) "
-                     f"x {reps} passes in {dt:.1f} s; plain C oracle, fp64 accumulation, OpenMP over rows"}
+                     f"x {reps} passes in {dt:.1f} s; plain C oracle, fp64 accumulation, OpenMP over rows",
+           "value_1_thread": round(layer_bytes * reps1 / dt1 / 1e9, 4),
+           "sample_1_thread": f"the same layer x {reps1} passes in {dt1:.1f} s on one thread"}
     nout = sum(e["N"] for e in host_layer0)
     parity = {"passed": ok, "checked": f"all {nout} outputs of decode layer 0 vs the CPU oracle",
               "max_err_over_tol": round(worst, 6)}

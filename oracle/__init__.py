@@ -16,6 +16,7 @@ Functions (each cites its passage in tq2_oracle.c):
   silu_mul(g, u)               -> h (fp64)
   gemm(codes, scales, N, K, X_bits[M][K]) -> Y[M][N] (one matvec per token)
   half_to_float(bits), float_to_half(value)
+  threads(), set_threads(n)
 """
 import ctypes
 import os
@@ -61,6 +62,8 @@ def _lib():
         lib.oracle_gemm.restype = None
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         _LIB = lib
     return _LIB
 
@@ -78,6 +81,11 @@ def _shape_check(N, K):
 def threads() -> int:
     """Threads the oracle's row loops use (OpenMP)."""
     return int(_lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's row loops from now on (OpenMP)."""
+    _lib().oracle_set_threads(int(n))
 
 
 def half_to_float(bits: int) -> float:

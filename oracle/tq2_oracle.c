@@ -237,8 +237,10 @@ void oracle_gemv_i8(const uint8_t *codes, const uint16_t *scales, int64_t N,
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_threads(void) { return 1; }
+void oracle_set_threads(int n) { (void)n; }
 #endif
 
 /* ---- output requantization (page "gemma4 wNa8o8 requires int8
