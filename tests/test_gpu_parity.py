@@ -515,3 +515,81 @@ def test_gemm_activation_ranges(tq2, kind):
     Yc = Y.cpu().numpy()
     for m in range(M):
         _check_f16(Yc[m], ref[m], _tol(s, X[m], N, K))
+
+
+def test_graph_capture_replay(tq2):
+    """The entry points captured in one HIP graph (torch's graph API) and
+    replayed three times, with new inputs copied into the captured buffers and
+    the same calls run eagerly between the replays: every replay equals the
+    eager result on the same inputs bit for bit (all kernels are
+    deterministic).  Covers the split-K batched path (workspace plus the
+    reduce kernel) and the two-tile batched path."""
+    (_, ca, sa, _), (_, cb, sb, _), (_, cc, scc, _) = (
+        _packed(2300, 256, 4096), _packed(2301, 4096, 16384), _packed(2302, 1000, 1280))
+    (dca, dsa), (dcb, dsb), (dcc, dsc) = _to_dev(ca, sa), _to_dev(cb, sb), _to_dev(cc, scc)
+    f16 = dict(dtype=torch.float16, device=DEV)
+    xa, xb = torch.empty(4096, **f16), torch.empty(16384, **f16)
+    Xb, Xc = torch.empty((20, 16384), **f16), torch.empty((5, 1280), **f16)
+    ya, ygu, hh = (torch.empty(256, device=DEV), torch.empty((2, 256), device=DEV),
+                   torch.empty(256, device=DEV))
+    yi8, Yb, Yc = torch.empty(4096, device=DEV), torch.empty((20, 4096), device=DEV), torch.empty(
+        (5, 1000), device=DEV)
+    wsb = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(4096, 16384, 20)), dtype=torch.uint8, device=DEV)
+    wsc = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(1000, 1280, 5)), dtype=torch.uint8, device=DEV)
+    assert tq2.tq2_gemm_workspace_bytes(4096, 16384, 20) > 0  # split K (and two tiles) in the graph
+    s_in = np.float32(0.03)
+
+    def run():
+        tq2.tq2_gemv(dca, dsa, xa, y=ya)
+        tq2.tq2_gemv_gate_up(dca, dsa, dca, dsa, xa, y=ygu)
+        tq2.tq2_gemv_gate_up_silu(dca, dsa, dca, dsa, xa, h=hh)
+        tq2.tq2_gemv_i8(dcb, dsb, xb, s_in, y=yi8)
+        tq2.tq2_gemm(dcb, dsb, Xb, y=Yb, ws=wsb)
+        tq2.tq2_gemm(dcc, dsc, Xc, y=Yc, ws=wsc)
+
+    outs = [ya, ygu, hh, yi8, Yb, Yc]
+
+    def fill(seed):
+        g = synth.rng(seed)
+        for t in (xa, xb, Xb, Xc):
+            vals = np.stack([synth.activations(g, t.shape[-1]) for _ in range(t.numel() // t.shape[-1])])
+            t.copy_(torch.from_numpy(vals.reshape(t.shape)))
+
+    fill(2310)
+    run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        fill(2320 + rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        run()
+        torch.cuda.synchronize()
+        for name, a, b in zip(["gemv", "gate_up", "silu", "i8", "gemm_splitk_2tile", "gemm"], got, outs):
+            assert torch.equal(a, b), (rep, name)
+
+
+def test_side_stream(tq2):
+    """Calls on a non-default stream (passed explicitly) give the same bits as
+    on the default stream."""
+    N, K, M = 4096, 4096, 3
+    _, c, s, x = _packed(2400, N, K)
+    dc, ds, xd = _to_dev(c, s, x)
+    X = torch.stack([xd, xd.flip(0), xd * 0.5]).contiguous()
+    y0 = tq2.tq2_gemv(dc, ds, xd)
+    Y0 = tq2.tq2_gemm(dc, ds, X)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    y1 = torch.empty_like(y0)
+    Y1 = torch.empty_like(Y0)
+    ws = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(N, K, M)), dtype=torch.uint8, device=DEV)
+    tq2.tq2_gemv(dc, ds, xd, y=y1, stream=st)
+    tq2.tq2_gemm(dc, ds, X, y=Y1, ws=ws, stream=st)
+    st.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    assert torch.equal(Y0, Y1)
