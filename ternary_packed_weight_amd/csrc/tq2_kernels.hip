@@ -438,9 +438,10 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
 
   // (1) loads: XP 16-weight groups of x per thread (two 16-byte reads each,
   //     coalesced across the workgroup; clamped, so unconditional), then
-  //     this wave's weights.  x goes first and stays first: the wait for it
-  //     counts loads in issue order, so weights issued before x would hold
-  //     the staging (and the barrier) until every weight had arrived.
+  //     the first kRowWindow rows of this wave's weights.  x goes first and
+  //     stays first: the wait for it counts loads in issue order, so weights
+  //     issued before x would hold the staging (and the barrier) until they
+  //     had arrived.
   // staging passes over the C*256 groups: the launcher guarantees
   // XP * blockDim >= C*256 (one pass for C <= 4, four for the runtime-C form)
   //     x is read through a buffer descriptor of exactly K elements, so the
@@ -1230,8 +1231,9 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
   const int ngroups = (int)(K / 16);
 
   // (1) loads: the activations first (XP groups of 16 per thread, clamped),
-  //     then the weights; x stays first so that waiting for it does not
-  //     wait for the weights (loads complete in issue order).
+  //     then the first kRowWindow rows of weights; x stays first so that
+  //     waiting for it does not wait for the weights (loads complete in
+  //     issue order).
   constexpr int XP = f16_stage_passes(CT);
   uint4 xa[XP], xb[XP];
   // range-checked: groups past K load as zeros (and quantize to 0)
