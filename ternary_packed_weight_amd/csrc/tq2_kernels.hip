@@ -434,7 +434,6 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   const int64_t kk = active ? k0 : 0;
   const int64_t row_bytes = K / 4;
   const int64_t BK = K / kBlock;
-  const int ngroups = (int)(K / 16);  // 16-weight groups to stage
 
   // (1) loads: XP 16-weight groups of x per thread (two 16-byte reads each,
   //     coalesced across the workgroup; clamped, so unconditional), then
@@ -1099,7 +1098,11 @@ __device__ __forceinline__ int64_t scaled_partial(uint16_t h, int P) {
   const int f = h & 1023;
   const int m = e ? (f | 1024) : f;
   const int sh = e ? e - 1 : 0;
-  int t = m * P;  // |m| < 2^11, |P| <= 2^13
+  // |m| < 2^11 and |P| <= 2^13: both fit 24-bit operands, which the sign
+  // extension makes visible to the compiler (one v_mul_i32_i24 instead of a
+  // quarter-rate 32-bit multiply); the product is exact
+  const int P24 = (int)((uint32_t)P << 8) >> 8;
+  int t = m * P24;
   if (h & 0x8000) t = -t;
   return (int64_t)t << sh;
 }
@@ -1174,7 +1177,7 @@ __device__ __forceinline__ float i8_epilogue(int64_t A, float s) {
 // LDS of the int8 matvec: x_q dwords [C][4][64] uint4, a sink uint4 for the
 // stores of threads with no group to stage, cross-wave sums [C*S][R] int64.
 __host__ __device__ inline size_t i8_lds_bytes(int C, int S, int R) {
-  return (size_t)C * 4 * 64 * 16 + 16 + (size_t)C * S * R * 8;
+  return (size_t)C * 4 * 64 * 16 + (size_t)C * 64 * 16 + 16 + (size_t)C * S * R * 8;
 }
 
 // Same work split as the fp16 matvec.  The workgroup quantizes the
@@ -1214,7 +1217,8 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
   extern __shared__ uint4 lds[];
   const int C = CT ? CT : sp.C, S = sp.S;
   uint4* xs = lds;                                                // [C][4][64]
-  uint4* sink = lds + C * 4 * 64;                                 // [1]
+  int* gsum = reinterpret_cast<int*>(lds + C * 4 * 64);           // [C][64][4] group sums of x_q
+  uint4* sink = lds + C * 4 * 64 + C * 64;                        // [1]
   int64_t* red = reinterpret_cast<int64_t*>(sink + 1);            // [C*S][R]
 
   const int tid = threadIdx.x;
@@ -1305,20 +1309,24 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
     }
     const int ch = m >> 8, ln = (m >> 2) & 63, gg = m & 3;
     *(staged ? xs + (ch * 4 + gg) * 64 + ln : sink) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    int gs = dot4(dw[0], 0x01010101u, 0);
+    gs = dot4(dw[1], 0x01010101u, gs);
+    gs = dot4(dw[2], 0x01010101u, gs);
+    gs = dot4(dw[3], 0x01010101u, gs);
+    *(staged ? gsum + (ch * 64 + ln) * 4 + gg : reinterpret_cast<int*>(sink)) = gs;
   }
   __syncthreads();
 
-  // (3) this lane's activations and seed -(sum of its 64 x_q)
+  // (3) this lane's activations and seed -(sum of its 64 x_q), from the
+  //     four group sums its stagers wrote
   uint32_t xq[16];
-  int seed = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint4 tt = xs[(c * 4 + i) * 64 + lane];
     xq[4 * i + 0] = tt.x; xq[4 * i + 1] = tt.y; xq[4 * i + 2] = tt.z; xq[4 * i + 3] = tt.w;
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) seed = dot4(xq[i], 0x01010101u, seed);
-  seed = -seed;
+  const int4 gs4 = reinterpret_cast<const int4*>(gsum)[c * 64 + lane];
+  const int seed = -((gs4.x + gs4.y) + (gs4.z + gs4.w));
 
   int64_t acc[R];
 #pragma unroll
