@@ -176,8 +176,14 @@ def cpu_leg(host_layer0, ys_layer0, min_seconds):
             break
     dt1 = time.perf_counter() - t1
     oracle.set_threads(cores)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     cpu = {"value": round(layer_bytes * reps / dt / 1e9, 4), "unit": "GB/s",
-           "cores": cores, "kind": "oracle",
+           "cores": cores, "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
            "sample": f"decode layer 0 (7 linears, {sum(e['N'] * e['K'] for e in host_layer0)} weights) "
                      f"x {reps} passes in {dt:.1f} s; plain C oracle, fp64 accumulation, OpenMP over rows",
            "value_1_thread": round(layer_bytes * reps1 / dt1 / 1e9, 4),
@@ -211,15 +217,16 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
     ("c1 q/o 4096x4096 fp16", 4096, 4096, "f16", 1001),
     ("c2 fused gate+up 2x16384x4096 fp16", 16384, 4096, "gate_up", 1003),
     ("c3 down 4096x16384 int8 (fused quantize)", 4096, 16384, "i8", 1004),
+    ("c3q down 4096x16384 int8, pre-quantized x_q (tq2_gemv_i8q)", 4096, 16384, "i8q", 1004),
     ("batched gate 16384x4096, 16 tokens per call (tq2_gemm)", 16384, 4096, "gemm16", 1005),
 ]
 ROTATION_BYTES = 1.1e9  # > the 256 MB Infinity Cache: every timed call streams from HBM
 
 
-def time_configs(torch, tq2, synth, reps=5):
+def time_configs(torch, tq2, synth, reps=10):
     """Per-call time of each single-call configuration: C rotating copies of
     the weights (>= 1.1 GB in all), up to 400 back-to-back calls captured as
-    one graph, median over `reps` replays.  Beside it, a read-only 16-byte
+    one graph, median and 95th percentile over `reps` replays.  Beside it, a read-only 16-byte
     stream kernel, one dispatch per call reading the call's weight bytes from
     a rotating pool of the same size: the achievable ceiling at that size,
     dispatch floor included."""
@@ -244,6 +251,8 @@ def time_configs(torch, tq2, synth, reps=5):
         nbytes = nmat * (N * K * 66 // 256 + 4 * N) + 2 * K  # x read once
         if kind == "gemm16":
             nbytes = N * K * 66 // 256 + 16 * (2 * K + 4 * N)  # weights once, 16 x and 16 y
+        if kind == "i8q":
+            nbytes = N * K * 66 // 256 + 4 * N + K  # x_q read once (1 byte per element)
         ncopy = max(2, int(np.ceil(ROTATION_BYTES / nbytes)))
         copies = [[(c.clone(), s.clone()) for (c, s) in mats] for _ in range(ncopy)]
         del mats
@@ -261,11 +270,16 @@ def time_configs(torch, tq2, synth, reps=5):
             ws16 = torch.empty(tq2.tq2_gemm_workspace_bytes(N, K, 16), dtype=torch.uint8, device="cuda")
             calls = [lambda j=j: tq2.tq2_gemm(copies[j][0][0], copies[j][0][1], X16, y=Y16, ws=ws16)
                      for j in range(ncall)]
+        elif kind == "i8q":
+            xq = tq2.tq2_quantize_i8(xs, sc)  # once, outside the timed calls
+            calls = [lambda j=j: tq2.tq2_gemv_i8q(copies[j][0][0], copies[j][0][1], xq, sc, y=y)
+                     for j in range(ncall)]
         else:
             calls = [lambda j=j: tq2.tq2_gemv_i8(copies[j][0][0], copies[j][0][1], xs, sc, y=y)
                      for j in range(ncall)]
         g = capture(torch, calls)
-        us = float(np.median([time_graph(torch, g, 1) / ncall for _ in range(reps)]))
+        ts = [time_graph(torch, g, 1) / ncall for _ in range(reps)]
+        us, us95 = float(np.median(ts)), float(np.percentile(ts, 95))
         del g, calls, copies
         torch.cuda.empty_cache()
 
@@ -284,14 +298,15 @@ def time_configs(torch, tq2, synth, reps=5):
         if kind == "gemm16":
             nbytes_tok = nbytes
             gbs = nbytes / us / 1e3
-            out[label] = {"us_per_call": round(us, 3), "tokens_per_s": round(16e6 / us, 1),
+            out[label] = {"us_per_call": round(us, 3), "us_per_call_p95": round(us95, 3),
+                          "tokens_per_s": round(16e6 / us, 1),
                           "weight_GB_s": round(gbs, 1), "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
                           "read_probe_us": round(us_rd, 3),
                           "speedup_vs_16_gemv": None, "bytes_per_call": int(nbytes_tok),
                           "rotation_copies": ncopy}
             log(f"{label}: {us:.2f} us/call, {16e6 / us:.0f} tokens/s, weights at {gbs:.1f} GB/s")
             continue
-        out[label] = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1),
+        out[label] = {"us_per_call": round(us, 3), "us_per_call_p95": round(us95, 3), "GB_s": round(gbs, 1),
                       "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
                       "read_probe_us": round(us_rd, 3), "read_probe_GB_s": round(rd_gbs, 1),
                       "pct_of_read_probe": round(100 * gbs / rd_gbs, 1),
