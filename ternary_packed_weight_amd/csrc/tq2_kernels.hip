@@ -1174,8 +1174,9 @@ __device__ __forceinline__ float i8_epilogue(int64_t A, float s) {
   return (float)((a * (double)s) * 0x1p-24);
 }
 
-// LDS of the int8 matvec: x_q dwords [C][4][64] uint4, a sink uint4 for the
-// stores of threads with no group to stage, cross-wave sums [C*S][R] int64.
+// LDS of the int8 matvec: x_q dwords [C][4][64] uint4, x_q group sums
+// [C][64][4] int32, a sink uint4 for the stores of threads with no group to
+// stage, cross-wave sums [C*S][R] int64.
 __host__ __device__ inline size_t i8_lds_bytes(int C, int S, int R) {
   return (size_t)C * 4 * 64 * 16 + (size_t)C * 64 * 16 + 16 + (size_t)C * S * R * 8;
 }
