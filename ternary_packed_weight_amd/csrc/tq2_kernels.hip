@@ -354,7 +354,7 @@ __device__ __forceinline__ RowPtr mapped_row(const MatSet& ms, int row0, int r, 
 }
 
 // Rows rb..re-1 only (rb, re compile-time after unrolling).
-template <int R, bool PAIR = false, bool SCALES = true>
+template <int R, bool PAIR = false>
 __device__ __forceinline__ void load_rows(const MatSet& ms, int row0, int64_t kk,
                                           int64_t row_bytes, int64_t BK, uint4 (&w)[R],
                                           uint16_t (&hs)[R], int rb, int re) {
@@ -368,26 +368,9 @@ __device__ __forceinline__ void load_rows(const MatSet& ms, int row0, int64_t kk
         v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc(rp.codes, (uint32_t)row_bytes), (int)coff, 0,
                                                    kNonTemporal));
     w[r] = make_uint4(t.x, t.y, t.z, t.w);
-    if constexpr (SCALES)
-      hs[r] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc(rp.scales, (uint32_t)(BK * 2)),
-                                                             (int)soff, 0, 0);
+    hs[r] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc(rp.scales, (uint32_t)(BK * 2)),
+                                                           (int)soff, 0, 0);
   }
-}
-
-// Block scales of a two-row wave in one load.  Lane l reads the scale of row
-// (l / 16) % 2 at block 16c + l % 16 (clamped to the row's last block), so
-// the value lane l needs for row r sits in lane 16r + l / 4 (moved there
-// with ds_bpermute).  One scale request per wave instead of one per row
-// (measured on MI355X: 256x4096 2.59 -> 2.40 us, 4096x4096 3.22 -> 3.17 us;
-// the same grouping over four rows was slower for the 4- and 8-row shapes).
-template <bool PAIR>
-__device__ __forceinline__ uint16_t load_scales_2rows(const MatSet& ms, int row0, int c,
-                                                      int64_t row_bytes, int64_t BK, int lane) {
-  int blk = c * 16 + (lane & 15);
-  blk = blk < (int)BK ? blk : (int)BK - 1;
-  const uint16_t* p0 = mapped_row<2, PAIR>(ms, row0, 0, row_bytes, BK).scales;
-  const uint16_t* p1 = mapped_row<2, PAIR>(ms, row0, 1, row_bytes, BK).scales;
-  return __builtin_nontemporal_load(((lane & 16) ? p1 : p0) + blk);
 }
 
 // Rows a wave keeps in flight.  The first kRowWindow rows are requested at
@@ -474,12 +457,9 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   }
   __builtin_amdgcn_sched_barrier(0);
   constexpr bool PAIR = EPI == kSiluMul;
-  constexpr bool SCALES2 = R == 2;  // both rows' scales in one load
   uint4 w[R];
   uint16_t hs[R];
-  uint16_t sc2 = 0;
-  if constexpr (SCALES2) sc2 = load_scales_2rows<PAIR>(ms, row0, c, row_bytes, BK, lane);
-  load_rows<R, PAIR, !SCALES2>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindow<R>);
+  load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindow<R>);
   __builtin_amdgcn_sched_barrier(0);
 
   // (2) stage: group m covers weights 16m..16m+15 = group (m % 4) of lane
@@ -539,15 +519,8 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   for (int r = 0; r < R; ++r) {
     if (r + kRowWindow<R> < R) {  // the next row into the window
       __builtin_amdgcn_sched_barrier(0);
-      load_rows<R, PAIR, !SCALES2>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindow<R>,
-                                   r + kRowWindow<R> + 1);
+      load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindow<R>, r + kRowWindow<R> + 1);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (SCALES2) {
-      if (r == 0) {
-        hs[0] = (uint16_t)__builtin_amdgcn_ds_bpermute((lane >> 2) * 4, (int)sc2);
-        hs[1] = (uint16_t)__builtin_amdgcn_ds_bpermute(((lane >> 2) + 16) * 4, (int)sc2);
-      }
     }
     const uint32_t keep = row_valid<R, PAIR>(ms, row0, r) ? 0xFFFFu : 0u;
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hs[r] & keep));
