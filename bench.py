@@ -226,7 +226,8 @@ WARM_REPLAYS = 5  # untimed graph replays (up to 2000 calls) before each configu
 
 def time_configs(torch, tq2, synth, reps=10):
     """Per-call time of each single-call configuration: C rotating copies of
-    the weights (>= 1.1 GB in all), up to 400 back-to-back calls captured as
+    the weights (>= 1.1 GB in all; x and y rotate with them), up to 400
+    back-to-back calls captured as
     one graph, median and 95th percentile over `reps` replays after
     WARM_REPLAYS untimed ones.  Beside it, a read-only 16-byte
     stream kernel, one dispatch per call reading the call's weight bytes from
@@ -259,31 +260,39 @@ def time_configs(torch, tq2, synth, reps=10):
         copies = [[(c.clone(), s.clone()) for (c, s) in mats] for _ in range(ncopy)]
         del mats
         ncall = min(ncopy, 400)
-        y = torch.empty(nmat * N, dtype=torch.float32, device="cuda")
+        # x and y rotate with the weights (one copy per call in the graph), so
+        # every call reads its activations from memory rather than from a
+        # cache that the previous call warmed
+        ys = [torch.empty(nmat * N, dtype=torch.float32, device="cuda") for _ in range(ncall)]
+        xr = [xs.clone() for _ in range(ncall)]
         sc = float(xs.float().abs().max() / 100)
         if kind == "f16":
-            calls = [lambda j=j: tq2.tq2_gemv(copies[j][0][0], copies[j][0][1], xs, y=y) for j in range(ncall)]
+            calls = [lambda j=j: tq2.tq2_gemv(copies[j][0][0], copies[j][0][1], xr[j], y=ys[j])
+                     for j in range(ncall)]
         elif kind == "gate_up":
             calls = [lambda j=j: tq2.tq2_gemv_gate_up(copies[j][0][0], copies[j][0][1], copies[j][1][0],
-                                                      copies[j][1][1], xs, y=y.view(2, N)) for j in range(ncall)]
+                                                      copies[j][1][1], xr[j], y=ys[j].view(2, N))
+                     for j in range(ncall)]
         elif kind == "gemm16":
             X16 = torch.stack([synth.torch_activations(seed + 1 + m, K) for m in range(16)])
-            Y16 = torch.empty(16, N, dtype=torch.float32, device="cuda")
+            X16r = [X16.clone() for _ in range(ncall)]
+            Y16 = [torch.empty(16, N, dtype=torch.float32, device="cuda") for _ in range(ncall)]
             ws16 = torch.empty(tq2.tq2_gemm_workspace_bytes(N, K, 16), dtype=torch.uint8, device="cuda")
-            calls = [lambda j=j: tq2.tq2_gemm(copies[j][0][0], copies[j][0][1], X16, y=Y16, ws=ws16)
+            calls = [lambda j=j: tq2.tq2_gemm(copies[j][0][0], copies[j][0][1], X16r[j], y=Y16[j], ws=ws16)
                      for j in range(ncall)]
         elif kind == "i8q":
             xq = tq2.tq2_quantize_i8(xs, sc)  # once, outside the timed calls
-            calls = [lambda j=j: tq2.tq2_gemv_i8q(copies[j][0][0], copies[j][0][1], xq, sc, y=y)
+            xqr = [xq.clone() for _ in range(ncall)]
+            calls = [lambda j=j: tq2.tq2_gemv_i8q(copies[j][0][0], copies[j][0][1], xqr[j], sc, y=ys[j])
                      for j in range(ncall)]
         else:
-            calls = [lambda j=j: tq2.tq2_gemv_i8(copies[j][0][0], copies[j][0][1], xs, sc, y=y)
+            calls = [lambda j=j: tq2.tq2_gemv_i8(copies[j][0][0], copies[j][0][1], xr[j], sc, y=ys[j])
                      for j in range(ncall)]
         g = capture(torch, calls)
         time_graph(torch, g, WARM_REPLAYS)  # untimed: steady state before the timed replays
         ts = [time_graph(torch, g, 1) / ncall for _ in range(reps)]
         us, us95 = float(np.median(ts)), float(np.percentile(ts, 95))
-        del g, calls, copies
+        del g, calls, copies, xr, ys
         torch.cuda.empty_cache()
 
         rb = (nmat * N * K * 66 // 256 + 255) // 256 * 256  # the call's weight bytes
