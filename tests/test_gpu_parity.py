@@ -261,6 +261,38 @@ def test_gate_up_full_size_sampled(tq2):
         _check_f16(yc[m, rows], ref, _tol(ss[rows], x, rows.size, K))
 
 
+def test_decode_step_sampled(tq2):
+    """The 224-linear decode step exactly as bench.py builds and times it
+    (weights packed by tq2_pack, one HIP graph, replayed): ten sampled rows of
+    every linear, re-drawn from the same seeds and packed by the oracle."""
+    import bench
+    stack, _ = bench.build_stack(tq2, synth, torch)
+    g = bench.capture(torch, [(lambda e=e: tq2.tq2_gemv(e["codes"], e["scales"], e["x"], y=e["y"]))
+                              for e in stack])
+    for e in stack:
+        e["y"].fill_(float("nan"))
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    sel = synth.rng(6)
+    worst = 0.0
+    for i, e in enumerate(stack):
+        l, p = divmod(i, len(bench.PROJ))
+        N, K = e["N"], e["K"]
+        q, d, _ = synth.torch_problem(10000 + 7 * l + p, N, K)
+        rows = np.unique(np.concatenate([sel.choice(N, 8, replace=False), [0, N - 1]]))
+        ri = torch.from_numpy(rows).to(DEV)
+        qh, dh = q[ri].cpu().numpy(), d[ri].cpu().numpy()
+        del q, d
+        x = e["x"].cpu().numpy()
+        codes, scales, bad = oracle.pack(_ternary_W(qh, dh))
+        assert bad == 0
+        ref = oracle.gemv(codes, scales, rows.size, K, synth.bits(x))
+        got = e["y"].cpu().numpy()[rows]
+        worst = max(worst, _check_f16(got, ref, _tol(scales, x, rows.size, K)))
+    assert worst <= 1.0
+
+
 # ------------------------------------------------------------ int8 path
 
 def test_quantize_bit_exact(tq2):
