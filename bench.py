@@ -19,7 +19,12 @@ back-to-back launches) and the CPU oracle
 timed on the host on a bounded sample (decode layer 0), which also serves as
 the parity gate: a mismatch prints passed=false and exits non-zero.
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu] [--probes]
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--probes] [--no-configs]
+                  [--config-calls C] [--config-reps R]
+
+--config-calls and --config-reps shrink the single-call configuration graphs
+for hardware-counter runs (every dispatch is then profiled); the figures of a
+normal run use the defaults.
 """
 import argparse
 import ctypes
@@ -224,7 +229,7 @@ ROTATION_BYTES = 1.1e9  # > the 256 MB Infinity Cache: every timed call streams 
 WARM_REPLAYS = 5  # untimed graph replays (up to 2000 calls) before each configuration's timed ones
 
 
-def time_configs(torch, tq2, synth, reps=10):
+def time_configs(torch, tq2, synth, reps=10, max_calls=400):
     """Per-call time of each single-call configuration: C rotating copies of
     the weights (>= 1.1 GB in all; x and y rotate with them), up to 400
     back-to-back calls captured as
@@ -259,7 +264,7 @@ def time_configs(torch, tq2, synth, reps=10):
         ncopy = max(2, int(np.ceil(ROTATION_BYTES / nbytes)))
         copies = [[(c.clone(), s.clone()) for (c, s) in mats] for _ in range(ncopy)]
         del mats
-        ncall = min(ncopy, 400)
+        ncall = min(ncopy, max_calls)
         # x and y rotate with the weights (one copy per call in the graph), so
         # every call reads its activations from memory rather than from a
         # cache that the previous call warmed
@@ -338,6 +343,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--probes", action="store_true", help="also run the byte-counter calibration kernels")
     ap.add_argument("--no-configs", action="store_true", help="skip the single-call configuration timings")
+    ap.add_argument("--config-calls", type=int, default=400,
+                    help="calls per configuration graph (fewer for hardware-counter runs)")
+    ap.add_argument("--config-reps", type=int, default=10, help="timed replays per configuration")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -397,7 +405,7 @@ def main():
 
     configs = None
     if not args.no_configs:
-        configs = time_configs(torch, tq2, synth)
+        configs = time_configs(torch, tq2, synth, reps=args.config_reps, max_calls=args.config_calls)
         for label, rec in configs.items():
             if "speedup_vs_16_gemv" in rec:  # same shape as the gate/up launches timed above
                 rec["speedup_vs_16_gemv"] = round(16 * us_dom / rec["us_per_call"], 2)
