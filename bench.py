@@ -224,7 +224,13 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
     ("c3 down 4096x16384 int8 (fused quantize)", 4096, 16384, "i8", 1004),
     ("c3q down 4096x16384 int8, pre-quantized x_q (tq2_gemv_i8q)", 4096, 16384, "i8q", 1004),
     ("batched gate 16384x4096, 16 tokens per call (tq2_gemm)", 16384, 4096, "gemm16", 1005),
+    # the adjacent entry points, each a single call on its own shape
+    ("next: fused q/k/v 4096+256+256 x 4096 fp16 (tq2_gemv_fused)", 4096, 4096, "qkv", 1006),
+    ("next: fused q/k/v 4096+256+256 x 4096 int8 (tq2_gemv_i8_fused)", 4096, 4096, "qkv_i8", 1006),
+    ("next: gate+up 2x16384x4096 with SiLU*mul epilogue (tq2_gemv_gate_up_silu)", 16384, 4096, "silu", 1003),
+    ("next: down 4096x16384 int8 with int8 output (tq2_gemv_i8_requant)", 4096, 16384, "requant", 1004),
 ]
+QKV_ROWS = (4096, 256, 256)
 ROTATION_BYTES = 1.1e9  # > the 256 MB Infinity Cache: every timed call streams from HBM
 WARM_REPLAYS = 5  # untimed graph replays (up to 2000 calls) before each configuration's timed ones
 
@@ -246,17 +252,22 @@ def time_configs(torch, tq2, synth, reps=10, max_calls=400):
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
     out = {}
     for label, N, K, kind, seed in CONFIGS:
-        nmat = 2 if kind == "gate_up" else 1
+        rows = QKV_ROWS if kind in ("qkv", "qkv_i8") else ((N, N) if kind in ("gate_up", "silu") else (N,))
+        nmat = len(rows)
         mats = []
         xs = None
-        for i in range(nmat):
-            q, d, x = synth.torch_problem(seed + 100 * i, N, K)
+        for i, Ni in enumerate(rows):
+            q, d, x = synth.torch_problem(seed + 100 * i, Ni, K)
             W = d.float().repeat_interleave(256, dim=1) * (q.float() - 1.0)
             c, s, _ = tq2.tq2_pack(W)
             del W, q, d
             mats.append((c, s))
             xs = x if xs is None else xs
-        nbytes = nmat * (N * K * 66 // 256 + 4 * N) + 2 * K  # x read once
+        nbytes = sum(Ni * K * 66 // 256 + 4 * Ni for Ni in rows) + 2 * K  # x read once
+        if kind == "silu":
+            nbytes = 2 * N * K * 66 // 256 + 2 * K + 4 * N  # h = silu(gate) * up written once
+        if kind == "requant":
+            nbytes = N * K * 66 // 256 + 2 * K + N  # int8 output
         if kind == "gemm16":
             nbytes = N * K * 66 // 256 + 16 * (2 * K + 4 * N)  # weights once, 16 x and 16 y
         if kind == "i8q":
@@ -268,7 +279,7 @@ def time_configs(torch, tq2, synth, reps=10, max_calls=400):
         # x and y rotate with the weights (one copy per call in the graph), so
         # every call reads its activations from memory rather than from a
         # cache that the previous call warmed
-        ys = [torch.empty(nmat * N, dtype=torch.float32, device="cuda") for _ in range(ncall)]
+        ys = [torch.empty(sum(rows), dtype=torch.float32, device="cuda") for _ in range(ncall)]
         xr = [xs.clone() for _ in range(ncall)]
         sc = float(xs.float().abs().max() / 100)
         if kind == "f16":
@@ -285,6 +296,19 @@ def time_configs(torch, tq2, synth, reps=10, max_calls=400):
             ws16 = torch.empty(tq2.tq2_gemm_workspace_bytes(N, K, 16), dtype=torch.uint8, device="cuda")
             calls = [lambda j=j: tq2.tq2_gemm(copies[j][0][0], copies[j][0][1], X16r[j], y=Y16[j], ws=ws16)
                      for j in range(ncall)]
+        elif kind == "qkv":
+            calls = [lambda j=j: tq2.tq2_gemv_fused(copies[j], xr[j], y=ys[j]) for j in range(ncall)]
+        elif kind == "qkv_i8":
+            calls = [lambda j=j: tq2.tq2_gemv_i8_fused(copies[j], xr[j], sc, y=ys[j]) for j in range(ncall)]
+        elif kind == "silu":
+            calls = [lambda j=j: tq2.tq2_gemv_gate_up_silu(copies[j][0][0], copies[j][0][1], copies[j][1][0],
+                                                           copies[j][1][1], xr[j], h=ys[j][:N])
+                     for j in range(ncall)]
+        elif kind == "requant":
+            yq = [torch.empty(N, dtype=torch.int8, device="cuda") for _ in range(ncall)]
+            calls = [lambda j=j: tq2.tq2_gemv_i8_requant(copies[j][0][0], copies[j][0][1], xr[j], sc, 0.05,
+                                                         y_q=yq[j], want_deq=False)
+                     for j in range(ncall)]
         elif kind == "i8q":
             xq = tq2.tq2_quantize_i8(xs, sc)  # once, outside the timed calls
             xqr = [xq.clone() for _ in range(ncall)]
@@ -300,7 +324,7 @@ def time_configs(torch, tq2, synth, reps=10, max_calls=400):
         del g, calls, copies, xr, ys
         torch.cuda.empty_cache()
 
-        rb = (nmat * N * K * 66 // 256 + 255) // 256 * 256  # the call's weight bytes
+        rb = (sum(rows) * K * 66 // 256 + 255) // 256 * 256  # the call's weight bytes
         pool = torch.ones(ncopy * rb, dtype=torch.uint8, device="cuda")
         st = ctypes.c_void_p
         rcalls = [lambda j=j: probe.tq2probe_read(st(pool.data_ptr() + j * rb), rb, st(sink.data_ptr()), 2048,
@@ -409,6 +433,11 @@ def main():
         for label, rec in configs.items():
             if "speedup_vs_16_gemv" in rec:  # same shape as the gate/up launches timed above
                 rec["speedup_vs_16_gemv"] = round(16 * us_dom / rec["us_per_call"], 2)
+        # the fused q/k/v call against three single calls of its shapes (c1 for q, c0 for k and v)
+        c0 = configs[CONFIGS[0][0]]["us_per_call"]
+        c1 = configs[CONFIGS[1][0]]["us_per_call"]
+        qkv = next(configs[label] for label, _, _, kind, _ in CONFIGS if kind == "qkv")
+        qkv["three_single_calls_us"] = round(c1 + 2 * c0, 3)
 
     cpu, parity = None, None
     if not args.no_cpu:
