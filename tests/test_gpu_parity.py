@@ -453,7 +453,7 @@ def test_fused_int8_bit_exact(tq2, Ns, K):
         off += N
 
 
-@pytest.mark.parametrize("N,K", [(1, 256), (7, 768), (2048, 4096), (16384, 4096), (130, 16384)])
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 768), (2048, 4096), (16384, 4096), (130, 16384), (9, 32768)])
 def test_gate_up_silu(tq2, N, K):
     """h = silu(g)*u against the oracle: g, u each within the fp16 tolerance
     and the fp32 epilogue within a few ulp."""
