@@ -34,6 +34,12 @@ def _hipcc(sources, out, verbose, extra=()):
     errs = [l for l in res.stderr.splitlines() if "error" in l]
     if errs:
         raise RuntimeError("\n".join(errs))
+    # a kernel whose host-side stub was dropped links without complaint and
+    # only fails at load time: refuse undefined symbols of our own namespace
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    own = [l.split()[-1] for l in und.stdout.splitlines() if "_ZN3tq2" in l]
+    if und.returncode != 0 or own:
+        raise RuntimeError(f"{out}: undefined library symbols: {own or und.stderr}")
     os.replace(tmp, out)
     return out
 

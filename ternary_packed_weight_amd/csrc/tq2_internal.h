@@ -54,6 +54,7 @@ hipError_t launch_gemv_i8_requant(const MatSet& m, int64_t K, const uint16_t* x,
 struct GemmPlan {
   int U, T, S;                // row groups per wave, steps per load batch, chunk-waves per workgroup
   int TT;                     // token tiles per wave
+  bool xl;                    // x staged through LDS (see k_gemm_mfma)
   int64_t mt, zt;             // 16-token tiles; groups of TT tiles (grid z)
   int64_t splits, steps_per_split, wgs;
   int64_t part_bytes;

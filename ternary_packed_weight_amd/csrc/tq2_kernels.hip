@@ -738,14 +738,48 @@ struct GemmArgs {
   int32_t steps_per_split;  // multiple of C*T
 };
 
+constexpr int kStepTile = kTok * kBlock * 2;  // x of one step for one tile: 8 KiB
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// the same for an n that is a constant once the caller's loops are unrolled
+template <int N = 63>
+__device__ __forceinline__ void wait_vm_at(int n) {
+  if (n == N) wait_vm<N>();
+  else if constexpr (N > 0) wait_vm_at<N - 1>(n);
+}
+// 16 bytes per lane from a buffer straight to LDS: lane l's bytes land at
+// lds + 16 l (lds wave-uniform)
+__device__ __forceinline__ void load_b128_lds(__amdgpu_buffer_rsrc_t r, int off, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0,
+                                           0, 0);
+}
+
 // Workgroup: C waves, the C chunks of one K-split of one row set (U row
 // groups) and TT token tiles; their sums meet in LDS and are added in chunk
 // order.  A wave decodes each code word once for all TT tiles (the A
 // operand is shared; each tile brings its own B operands).  Grid: (row sets,
 // K-splits, token tiles / TT).
-template <int U, int T, int C, int TT>
+//
+// x reaches the lanes one of two ways.  XL: straight to LDS, each load
+// instruction bringing two tokens' 512 contiguous bytes of a step (every
+// cache line read by one instruction), then read back in operand order.
+// Otherwise: each lane loads its own token's 64 values of the step, so one
+// instruction touches 64 cache lines and each line is touched by eight
+// instructions, which stalls issue once the tile is full; with few tokens
+// there is little to stall and the LDS round trip costs more.
+template <int U, int T, int C, int TT, bool XL>
 __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
-  __shared__ float red[C][TT][U][4][64];
+  // XL: per wave, the x of its load batch (T steps x TT tiles of 8 KiB);
+  // after the loop the same memory holds the chunk sums
+  constexpr int kXBytes = XL ? C * T * TT * kStepTile : 0;
+  constexpr int kRedBytes = C * TT * U * 4 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kXBytes > kRedBytes ? kXBytes : kRedBytes];
+  float(*red)[TT][U][4][64] = reinterpret_cast<float(*)[TT][U][4][64]>(smem);
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4, i = lane & 15;
   const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -794,14 +828,30 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
     // read zeros (or are not used); tokens past M read zeros through their
     // tile's descriptor.
     uint4 xv[TT][T][8];
+    uint8_t* xs = smem + c * (T * TT * kStepTile);  // XL: this wave's x
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int s = s0 + t < s_end ? s0 + t : s0;  // in range
-      const int xoff = (int)((i * a.K + 256 * (int64_t)s + 64 * G) * 2);
+      if constexpr (XL) {
+        // load n of a step-tile: tokens 2n + (lane >> 5); lane l stores chunk
+        // (l & 31) ^ token (16 bytes) of its token at position l & 31, which
+        // puts the 16 tokens of one later read in distinct banks
 #pragma unroll
-      for (int q = 0; q < TT; ++q)
+        for (int q = 0; q < TT; ++q)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) xv[q][t][k] = load_b128(xr[q], xoff + 16 * k);
+          for (int n = 0; n < 8; ++n) {
+            const int tok = 2 * n + (lane >> 5);
+            const int ch = (lane & 31) ^ tok;
+            const int off = (int)((tok * a.K + 256 * (int64_t)s + 8 * ch) * 2);
+            load_b128_lds(xr[q], off, xs + (t * TT + q) * kStepTile + 1024 * n);
+          }
+      } else {
+        const int xoff = (int)((i * a.K + 256 * (int64_t)s + 64 * G) * 2);
+#pragma unroll
+        for (int q = 0; q < TT; ++q)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) xv[q][t][k] = load_b128(xr[q], xoff + 16 * k);
+      }
     }
     uint4 w[T][U];
     uint16_t d[T][U][4];
@@ -840,10 +890,22 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < TT; ++q) {
         uint32_t xw[32];
+        if constexpr (XL) {
+          // this step's x is in LDS once the loads issued after it are all
+          // that is left in flight (its later steps, the codes, the scales)
+          if (q == 0) wait_vm_at((T - 1 - t) * TT * 8 + 5 * T * U);
+          const uint8_t* xl = xs + (t * TT + q) * kStepTile + 512 * i;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          xw[4 * k] = xv[q][t][k].x; xw[4 * k + 1] = xv[q][t][k].y;
-          xw[4 * k + 2] = xv[q][t][k].z; xw[4 * k + 3] = xv[q][t][k].w;
+          for (int k = 0; k < 8; ++k) {
+            const uint4 e = *reinterpret_cast<const uint4*>(xl + 16 * ((8 * G + k) ^ i));
+            xw[4 * k] = e.x; xw[4 * k + 1] = e.y; xw[4 * k + 2] = e.z; xw[4 * k + 3] = e.w;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            xw[4 * k] = xv[q][t][k].x; xw[4 * k + 1] = xv[q][t][k].y;
+            xw[4 * k + 2] = xv[q][t][k].z; xw[4 * k + 3] = xv[q][t][k].w;
+          }
         }
         // block sums of x and x^2 (the four lanes of a token hold its block)
         float s0f = 0.0f, s1f = 0.0f, q0f = 0.0f, q1f = 0.0f;
@@ -917,6 +979,7 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
 
   // chunk sums meet in LDS; wave 0 adds them in chunk order and stores
   if (C > 1) {
+    if constexpr (XL) __syncthreads();  // all x reads done before the sums overwrite it
 #pragma unroll
     for (int q = 0; q < TT; ++q)
 #pragma unroll
@@ -976,6 +1039,13 @@ GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
   // save (256x4096 at 32 tokens 7.2 -> 9.2 us), so they keep one tile.
   p.TT = (p.mt >= 2 && rsets * steps >= 4096) ? 2 : 1;
   p.zt = (p.mt + p.TT - 1) / p.TT;
+  // x through LDS once the tile holds enough tokens for the scattered
+  // per-lane loads to stall (measured on MI355X, same box: 16384x4096 at 16
+  // tokens 12.2 -> 10.1 us, 4096x16384 at 16 14.6 -> 12.9, at 4 tokens
+  // 10.2 -> 9.6 and 12.6 -> 12.3; 4096x4096 and 256x4096 lose 0.1-0.3 us
+  // at up to 8 tokens, and every shape loses at 1-2 tokens).  Two-tile waves
+  // (more than 16 tokens) always take it.
+  p.xl = M > 8 || (M >= 4 && rsets * steps >= 4096);
   // Measured on MI355X: when the row sets alone fill the CUs, or K is long
   // (>= 8192), 8 chunk-waves per workgroup with 2 steps per load batch;
   // otherwise (few rows, short K: K is split across workgroups anyway) 4
@@ -1019,14 +1089,20 @@ hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, 
   a.M = M;
   a.steps_per_split = (int32_t)p.steps_per_split;
   const dim3 grid((unsigned)p.wgs, (unsigned)p.splits, (unsigned)p.zt);
-  if (p.TT == 2)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 2>), grid, dim3(64 * 4), 0, st, a);
+  if (p.TT == 2)  // implies xl
+    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 2, true>), grid, dim3(64 * 4), 0, st, a);
+  else if (p.T == 2 && p.S == 8 && p.xl)
+    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 8, 1, true>), grid, dim3(64 * 8), 0, st, a);
   else if (p.T == 2 && p.S == 8)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 8, 1>), grid, dim3(64 * 8), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 8, 1, false>), grid, dim3(64 * 8), 0, st, a);
+  else if (p.T == 2 && p.xl)
+    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 4, 1, true>), grid, dim3(64 * 4), 0, st, a);
   else if (p.T == 2)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 4, 1>), grid, dim3(64 * 4), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 4, 1, false>), grid, dim3(64 * 4), 0, st, a);
+  else if (p.xl)
+    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 1, true>), grid, dim3(64 * 4), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 1>), grid, dim3(64 * 4), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 1, false>), grid, dim3(64 * 4), 0, st, a);
   if (p.splits > 1) {
     const int64_t MN = M * N;
     hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, part,

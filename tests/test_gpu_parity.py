@@ -515,7 +515,9 @@ def test_gemm_parity(tq2, N, K, M):
 
 def test_gemm_token_independence_and_determinism(tq2):
     """A token's output does not depend on the other tokens of the call, and
-    repeated calls are bitwise identical (split partials added in order)."""
+    repeated calls are bitwise identical (split partials added in order).
+    16 tokens stage x through LDS, 1 token loads it per lane: the two ways
+    must give the same bits."""
     N, K = 4096, 16384
     _, c, s, _ = _packed(1950, N, K)
     g = synth.rng(1951)
@@ -532,11 +534,13 @@ def test_gemm_token_independence_and_determinism(tq2):
     _check_f16(Y1[5].cpu().numpy(), Yv.cpu().numpy().astype(np.float64), 2 * _tol(s, X[5], N, K))
 
 
+@pytest.mark.parametrize("M", [3, 17])
 @pytest.mark.parametrize("kind", RANGE_KINDS)
-def test_gemm_activation_ranges(tq2, kind):
+def test_gemm_activation_ranges(tq2, kind, M):
     """The batched path scales its B operands per (token, block); tiny
-    activations must come through exactly and large ones within tolerance."""
-    N, K, M = 300, 4352, 3
+    activations must come through exactly and large ones within tolerance.
+    3 tokens: x loaded per lane; 17: x staged through LDS, two tiles."""
+    N, K = 300, 4352
     _, c, s, _ = _packed(2200, N, K)
     g = synth.rng(2201)
     X = np.stack([_range_activations(kind, K, g) for _ in range(M)])
