@@ -1050,17 +1050,25 @@ GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
   // (>= 8192), 8 chunk-waves per workgroup with 2 steps per load batch;
   // otherwise (few rows, short K: K is split across workgroups anyway) 4
   // chunk-waves with 1 step per batch, which keeps each wave's
-  // load-then-compute chain short.  Splits double until ~8 waves per CU or
-  // until every wave would get fewer than T steps.
+  // load-then-compute chain short.
+  //
+  // K splits (each adds its partials to the workspace traffic and needs the
+  // reduce launch) double while the workgroups still fit one per CU and
+  // every wave keeps at least T steps.  Measured on MI355X, same box: the
+  // former rule (double until 8 waves per CU) split 16384x4096 at 17-32
+  // tokens into 512 workgroups, 15.8-17.6 us against 13.9-14.1 unsplit;
+  // 4096x16384 at 17-32 tokens 18.8-19.3 (512) against 16.6-17.6 (256);
+  // 4096x4096 at 48 tokens 11.5 (768) against 9.6 (192).  Below one
+  // workgroup per CU splitting pays: 4096x16384 at 16 tokens 24.6 us
+  // unsplit, 17.2 at 2 splits, 11.9 at 4.
   const bool wide = rsets * p.zt >= device_cus() || steps >= 32;
   p.T = (wide && p.TT == 1) ? 2 : 1;
   p.S = (wide && steps >= 16 && p.TT == 1) ? 8 : 4;  // two tiles: 4 waves (registers)
   const int64_t per_split = (int64_t)p.S * p.T;
-  const int64_t target = 8LL * device_cus();
   int64_t max_splits = steps / per_split;
   if (max_splits < 1) max_splits = 1;
   int64_t splits = 1;
-  while (splits * 2 <= max_splits && rsets * p.zt * splits * p.S < target) splits *= 2;
+  while (splits * 2 <= max_splits && rsets * p.zt * splits * 2 <= device_cus()) splits *= 2;
   int64_t sps = (steps + splits - 1) / splits;
   sps = (sps + per_split - 1) / per_split * per_split;
   p.splits = (steps + sps - 1) / sps;
