@@ -613,7 +613,8 @@ static int device_cus() {
 // Waves per workgroup: C chunk-waves for each of S row groups (measured on
 // MI355X).  fp16, one chunk (K <= 4096): 4-wave workgroups.  Otherwise 8
 // waves when C divides 8, except K = 16384 (C = 4), where 16-wave workgroups
-// halve the activation staging per row.
+// halve the activation staging per row.  (The int8 launcher may take 4-wave
+// workgroups at one chunk as well, by how the row groups fill the CUs.)
 static Split pick_split(int64_t K, bool fp16) {
   const int C = (int)chunks_of(K);
   Split sp;
@@ -1490,8 +1491,16 @@ template <int R, bool QUANT, bool PARTIALS, bool REQUANT>
 static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
                               float s, float* y, int32_t* partials, const Requant& rq,
                               hipStream_t st) {
-  const Split sp = pick_split(K, false);
+  Split sp = pick_split(K, false);
   const int64_t groups = (m.rows + R - 1) / R;
+  if (sp.C == 1) {
+    // 8 or 4 row groups per workgroup, whichever leaves fewer on the
+    // busiest CU (8 on a tie).  Measured on MI355X, same box: q/k/v fused
+    // (4608 rows, 288 workgroups of 8) 4.30 -> 3.92 us with 4; 256 rows
+    // 3.04 -> 2.87; 4096 rows (256 workgroups of 8) 3.33 against 3.55.
+    const int64_t cus = device_cus(), w8 = (groups + 7) / 8, w4 = (groups + 3) / 4;
+    if ((w4 + cus - 1) / cus * 4 < (w8 + cus - 1) / cus * 8) sp.S = 4;
+  }
   const int64_t grid = (groups + sp.S - 1) / sp.S;
   const size_t lds = i8_lds_bytes(sp.C, sp.S, R);
   const dim3 g((unsigned)grid), b(64 * sp.C * sp.S);
