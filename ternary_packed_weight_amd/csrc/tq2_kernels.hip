@@ -824,10 +824,11 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
 
   for (int s0 = s_begin; s0 < s_end; s0 += T) {
     // issue, in this order (loads complete in issue order): the x of up to
-    // T steps for each tile (64 values of this lane's token per step, L2),
-    // then the code words (HBM), then the scales.  Steps past the range
-    // read zeros (or are not used); tokens past M read zeros through their
-    // tile's descriptor.
+    // T steps for each tile (L2; XL: into LDS, two tokens per load,
+    // otherwise this lane's token's 64 values per step into registers), then
+    // the code words (HBM), then the scales.  Steps past the range read
+    // zeros (or are not used); tokens past M read zeros through their tile's
+    // descriptor.
     uint4 xv[TT][T][8];
     uint8_t* xs = smem + c * (T * TT * kStepTile);  // XL: this wave's x
 #pragma unroll
@@ -854,6 +855,7 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
           for (int k = 0; k < 8; ++k) xv[q][t][k] = load_b128(xr[q], xoff + 16 * k);
       }
     }
+    if constexpr (XL) __builtin_amdgcn_sched_barrier(0);  // keeps the order the wait counts on
     uint4 w[T][U];
     uint16_t d[T][U][4];
 #pragma unroll
