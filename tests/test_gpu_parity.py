@@ -492,7 +492,9 @@ def test_int8_requant_bit_exact(tq2, N, K, div_in, s_out):
 
 GEMM_SHAPES = [(256, 4096, 16), (33, 768, 5), (4096, 4096, 2), (1000, 1280, 17), (64, 256, 1),
                (4096, 16384, 16), (16384, 4096, 8), (7, 65280, 3), (300, 4352, 33),
-               (4096, 16384, 20), (16384, 4096, 40)]
+               (4096, 16384, 20), (16384, 4096, 40),
+               (16384, 4096, 4),   # fewest tokens that stage x through LDS on a large shape
+               (300, 4352, 100)]   # seven token tiles, the last one ragged
 
 
 @pytest.mark.parametrize("N,K,M", GEMM_SHAPES)
