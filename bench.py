@@ -19,8 +19,14 @@ back-to-back launches) and the CPU oracle
 timed on the host on a bounded sample (decode layer 0), which also serves as
 the parity gate: a mismatch prints passed=false and exits non-zero.
 
+Beside it, `step_fused`: the same weights called as a layer shares its
+inputs (q, k, v in one fused call on one x; gate and up in one call; o and
+down alone: 128 launches), with layer 0 checked bit for bit against single
+calls on the same inputs.  It is reported, not the metric: the metric's step
+gives every linear its own x.
+
   python bench.py [--steps K] [--warmup W] [--no-cpu] [--probes] [--no-configs]
-                  [--config-calls C] [--config-reps R]
+                  [--no-fused-step] [--config-calls C] [--config-reps R]
 
 --config-calls and --config-reps shrink the single-call configuration graphs
 for hardware-counter runs (every dispatch is then profiled); the figures of a
@@ -235,6 +241,46 @@ ROTATION_BYTES = 1.1e9  # > the 256 MB Infinity Cache: every timed call streams 
 WARM_REPLAYS = 5  # untimed graph replays (up to 2000 calls) before each configuration's timed ones
 
 
+def fused_step(torch, tq2, stack, steps):
+    """The same 224 weights as the step, called the way a model's layer
+    shares its inputs: q, k and v in one tq2_gemv_fused call on one x, o
+    alone, gate and up in one tq2_gemv_gate_up call on one x, down alone
+    (4 launches per layer).  Layer 0's outputs must equal single tq2_gemv
+    calls on the same inputs bit for bit."""
+    layers = [stack[i:i + len(PROJ)] for i in range(0, len(stack), len(PROJ))]
+    bufs, launches, nbytes = [], [], 0
+    for q, k, v, o, g, u, d in layers:
+        yqkv = torch.empty(q["N"] + k["N"] + v["N"], dtype=torch.float32, device="cuda")
+        ygu = torch.empty(2, g["N"], dtype=torch.float32, device="cuda")
+        mats = [(q["codes"], q["scales"]), (k["codes"], k["scales"]), (v["codes"], v["scales"])]
+        launches += [lambda mats=mats, x=q["x"], y=yqkv: tq2.tq2_gemv_fused(mats, x, y=y),
+                     lambda e=o: tq2.tq2_gemv(e["codes"], e["scales"], e["x"], y=e["y"]),
+                     lambda g=g, u=u, y=ygu: tq2.tq2_gemv_gate_up(g["codes"], g["scales"], u["codes"],
+                                                                  u["scales"], g["x"], y=y),
+                     lambda e=d: tq2.tq2_gemv(e["codes"], e["scales"], e["x"], y=e["y"])]
+        bufs.append((yqkv, ygu))
+        w = sum(e["N"] * e["K"] * 66 // 256 for e in (q, k, v, o, g, u, d))
+        nbytes += w + 2 * (q["K"] + o["K"] + g["K"] + d["K"]) + 4 * sum(e["N"] for e in (q, k, v, o, g, u, d))
+    graph = capture(torch, launches)
+    time_graph(torch, graph, 3)
+    us = time_graph(torch, graph, steps)
+    q, k, v, o, g, u, d = layers[0]
+    yqkv, ygu = bufs[0]
+    ref = torch.cat([tq2.tq2_gemv(e["codes"], e["scales"], q["x"]) for e in (q, k, v)])
+    ref_gu = torch.stack([tq2.tq2_gemv(e["codes"], e["scales"], g["x"]) for e in (g, u)])
+    torch.cuda.synchronize()
+    same = bool(torch.equal(yqkv, ref) and torch.equal(ygu, ref_gu))
+    log(f"fused step: {us:.1f} us ({1e6 / us:.0f} steps/s), {nbytes / us / 1e3:.1f} GB/s; "
+        f"layer 0 equal to single calls: {same}")
+    if not same:
+        raise RuntimeError("fused calls differ from single calls on layer 0")
+    return {"us_per_step": round(us, 1), "steps_per_s": round(1e6 / us, 1),
+            "GB_s": round(nbytes / us / 1e3, 1), "bytes_per_step": nbytes,
+            "launches_per_step": len(launches), "layer0_equals_single_calls": same,
+            "calls": "per layer: tq2_gemv_fused(q,k,v; one x), tq2_gemv(o), "
+                     "tq2_gemv_gate_up(gate,up; one x), tq2_gemv(down)"}
+
+
 def time_configs(torch, tq2, synth, reps=10, max_calls=400):
     """Per-call time of each single-call configuration: C rotating copies of
     the weights (>= 1.1 GB in all; x and y rotate with them), up to 400
@@ -370,6 +416,7 @@ def main():
     ap.add_argument("--config-calls", type=int, default=400,
                     help="calls per configuration graph (fewer for hardware-counter runs)")
     ap.add_argument("--config-reps", type=int, default=10, help="timed replays per configuration")
+    ap.add_argument("--no-fused-step", action="store_true", help="skip the step built from the fused calls")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -420,6 +467,8 @@ def main():
                 "launches_timed": len(dom), "kernel_source_sha": sha}
     log(f"dominant kernel: {us_dom:.2f} us/launch, {achieved:.1f} GB/s ({achieved / PEAK_HBM_GBS:.1%})")
 
+    step_fused = None if args.no_fused_step else fused_step(torch, tq2, stack, args.steps)
+
     if args.probes:
         # eager launches too, so per-dispatch counters see the dominant kernel
         for e in dom:
@@ -458,6 +507,7 @@ def main():
         "steps_per_s": round(1e6 / us_step, 1),
         "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
         "roofline": roofline,
+        "step_fused": step_fused,
         "configs": configs,
         "cpu_baseline": cpu,
         "parity": parity,
