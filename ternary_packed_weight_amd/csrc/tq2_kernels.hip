@@ -895,7 +895,9 @@ __global__ __launch_bounds__(64 * C) void k_gemm_mfma(GemmArgs a) {
         uint32_t xw[32];
         if constexpr (XL) {
           // this step's x is in LDS once the loads issued after it are all
-          // that is left in flight (its later steps, the codes, the scales)
+          // that is left in flight (its later steps, the codes, the scales).
+          // The compiler also orders LDS reads after the LDS-bound loads (it
+          // waits for all of them), so this is the bound, not the only guard.
           if (q == 0) wait_vm_at((T - 1 - t) * TT * 8 + 5 * T * U);
           const uint8_t* xl = xs + (t * TT + q) * kStepTile + 512 * i;
 #pragma unroll
