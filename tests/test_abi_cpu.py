@@ -191,3 +191,19 @@ def test_gemm_workspace_only_for_split_k(tq2):
     assert lib.tq2_gemm_workspace_bytes(16384, 4096, 16) == 0
     assert lib.tq2_gemm_workspace_bytes(256, 4096, 16) % (4 * 16 * 256) == 0
     assert lib.tq2_gemm_workspace_bytes(256, 4096, 16) > 0
+
+
+@no_gpu
+def test_gemm_split_rule(tq2):
+    """K is split only while the workgroups still fit one per CU (256 CUs):
+    the workspace is splits x M x N fp32 partials, or 0 without a split."""
+    lib = tq2.lib()
+    ws = lib.tq2_gemm_workspace_bytes
+    assert ws(16384, 4096, 32) == 0                 # 256 row sets, two tiles per wave
+    assert ws(16384, 4096, 64) == 0                 # 512 workgroups already
+    assert ws(4096, 4096, 48) == 0                  # 192 workgroups: a split would make 384
+    assert ws(4096, 16384, 16) == 4 * 16 * 4096 * 4  # 64 row sets -> 4 splits
+    assert ws(4096, 16384, 32) == 4 * 32 * 4096 * 4
+    assert ws(4096, 16384, 48) == 2 * 48 * 4096 * 4  # 128 workgroups -> 2 splits
+    assert ws(4096, 4096, 16) == 4 * 16 * 4096 * 4   # 64 -> 4 (every wave keeps its step)
+    assert ws(4096, 4096, 32) == 2 * 32 * 4096 * 4   # 128 -> 2
