@@ -531,6 +531,12 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
       load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindow<R>, r + kRowWindow<R> + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // once its last row is requested the wave only decodes and stores: a
+    // higher issue priority lets it finish ahead of waves still starting
+    // (measured on MI355X, each time both builds on one box, two boxes:
+    // decode step 911-915 -> 904-908 us; the gate/up launches alone and the
+    // single-shape calls unchanged)
+    if (r == R - kRowWindow<R>) __builtin_amdgcn_s_setprio(1);
     const uint32_t keep = row_valid<R, PAIR>(ms, row0, r) ? 0xFFFFu : 0u;
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hs[r] & keep));
     acc[r] = __builtin_fmaf((float)d, lane_dot_f16(w[r], xp, seed), 0.0f);  // v_fma_mix
