@@ -427,6 +427,14 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   uint4* sink = reinterpret_cast<uint4*>(gsum + C * 64);        // [3]
   float* red = reinterpret_cast<float*>(sink + 3);              // [C*S][R]
 
+  // issue priority: 2 while the wave stages x and requests its first rows
+  // (a wave that is starting gets its requests out ahead of waves that are
+  // decoding), 0 while it decodes with rows in flight, 1 once its last row
+  // is requested.  Measured on MI355X, each time both builds on one box:
+  // the start priority took the decode step 905-911 -> 884-886 us and the
+  // gate/up launches back to back 5.55 -> 5.34 us; the tail priority alone
+  // took the step 911-915 -> 904-908 us (single-shape calls unchanged).
+  __builtin_amdgcn_s_setprio(2);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave-uniform indices, kept in scalar registers
@@ -470,6 +478,7 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   uint16_t hs[R];
   load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindow<R>);
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
 
   // (2) stage: group m covers weights 16m..16m+15 = group (m % 4) of lane
   //     (m / 4) % 64 of chunk m / 256.  Its 8 operand pairs go to slots
@@ -531,12 +540,7 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
       load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindow<R>, r + kRowWindow<R> + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // once its last row is requested the wave only decodes and stores: a
-    // higher issue priority lets it finish ahead of waves still starting
-    // (measured on MI355X, each time both builds on one box, two boxes:
-    // decode step 911-915 -> 904-908 us; the gate/up launches alone and the
-    // single-shape calls unchanged)
-    if (r == R - kRowWindow<R>) __builtin_amdgcn_s_setprio(1);
+    if (r == R - kRowWindow<R>) __builtin_amdgcn_s_setprio(1);  // only decoding is left
     const uint32_t keep = row_valid<R, PAIR>(ms, row0, r) ? 0xFFFFu : 0u;
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hs[r] & keep));
     acc[r] = __builtin_fmaf((float)d, lane_dot_f16(w[r], xp, seed), 0.0f);  // v_fma_mix
