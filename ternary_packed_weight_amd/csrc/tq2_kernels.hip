@@ -381,6 +381,12 @@ __device__ __forceinline__ void load_rows(const MatSet& ms, int row0, int64_t kk
 // 4096x16384 6.45 -> 5.95 us; windows of 2 or 6 of 8 rows were slower).
 template <int R>
 constexpr int kRowWindow = R >= 8 ? 4 : (R >= 4 ? 2 : R);
+// The fp16 matvec, with its issue priorities (a starting wave requests ahead
+// of decoding ones), does best with 5 of 8 (measured on MI355X, same box:
+// decode step 882.9 -> 878.2 us, gate/up back to back 5.34 -> 5.25 us; 3 and
+// 6 of 8, and 3 of 4, were slower).
+template <int R>
+constexpr int kRowWindowF16 = R >= 8 ? 5 : kRowWindow<R>;
 
 struct Split {
   int C;  // chunk-waves per row group
@@ -476,7 +482,7 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   constexpr bool PAIR = EPI == kSiluMul;
   uint4 w[R];
   uint16_t hs[R];
-  load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindow<R>);
+  load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindowF16<R>);
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(0);
 
@@ -535,12 +541,12 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r + kRowWindow<R> < R) {  // the next row into the window
+    if (r + kRowWindowF16<R> < R) {  // the next row into the window
       __builtin_amdgcn_sched_barrier(0);
-      load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindow<R>, r + kRowWindow<R> + 1);
+      load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindowF16<R>, r + kRowWindowF16<R> + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (r == R - kRowWindow<R>) __builtin_amdgcn_s_setprio(1);  // only decoding is left
+    if (r == R - kRowWindowF16<R>) __builtin_amdgcn_s_setprio(1);  // only decoding is left
     const uint32_t keep = row_valid<R, PAIR>(ms, row0, r) ? 0xFFFFu : 0u;
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hs[r] & keep));
     acc[r] = __builtin_fmaf((float)d, lane_dot_f16(w[r], xp, seed), 0.0f);  // v_fma_mix
