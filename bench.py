@@ -262,7 +262,7 @@ def fused_step(torch, tq2, stack, steps):
         w = sum(e["N"] * e["K"] * 66 // 256 for e in (q, k, v, o, g, u, d))
         nbytes += w + 2 * (q["K"] + o["K"] + g["K"] + d["K"]) + 4 * sum(e["N"] for e in (q, k, v, o, g, u, d))
     graph = capture(torch, launches)
-    time_graph(torch, graph, 3)
+    time_graph(torch, graph, 20)  # untimed warm-up replays
     us = time_graph(torch, graph, steps)
     q, k, v, o, g, u, d = layers[0]
     yqkv, ygu = bufs[0]
@@ -407,8 +407,8 @@ def time_configs(torch, tq2, synth, reps=10, max_calls=400):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg (and its parity gate)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--probes", action="store_true", help="also run the byte-counter calibration kernels")
@@ -454,7 +454,7 @@ def main():
     # ---- dominant kernel: the gate and up launches back to back
     dom = [e for e in stack if e["name"] in DOMINANT]
     dom_graph = capture(torch, [launch(e) for e in dom])
-    time_graph(torch, dom_graph, 5)  # untimed warm-up replays
+    time_graph(torch, dom_graph, 20)  # untimed warm-up replays
     us_dom = time_graph(torch, dom_graph, max(3, args.steps // 2)) / len(dom)
     dom_bytes = sum(algo_bytes(e["N"], e["K"]) for e in dom) / len(dom)
     achieved = dom_bytes / us_dom / 1e3
