@@ -51,7 +51,7 @@ PROJ = [("q", 4096, 4096), ("k", 256, 4096), ("v", 256, 4096), ("o", 4096, 4096)
 # launches of the dominant kernel: gate and up (16384x4096) both run
 # tq2::k_gemv_f16<8, 1, 512, 0> (8 rows per wave, one 4096-wide chunk)
 DOMINANT = ("gate", "up")
-DOMINANT_KERNEL = "tq2::k_gemv_f16<8, 1, 512, 0> (gate and up, 16384x4096)"
+DOMINANT_KERNEL = "tq2::k_gemv_f16<8, 1, 512, 0, true> (gate and up, 16384x4096)"
 TRAFFIC_FILE = "gemv_f16_gate_up_16384x4096_traffic.json"
 METRIC = "tq2_gemv achieved HBM GB/s and % of MI355X peak; 224-linear decode steps/sec"
 

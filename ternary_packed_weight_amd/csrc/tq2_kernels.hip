@@ -381,12 +381,6 @@ __device__ __forceinline__ void load_rows(const MatSet& ms, int row0, int64_t kk
 // 4096x16384 6.45 -> 5.95 us; windows of 2 or 6 of 8 rows were slower).
 template <int R>
 constexpr int kRowWindow = R >= 8 ? 4 : (R >= 4 ? 2 : R);
-// The fp16 matvec, with its issue priorities (a starting wave requests ahead
-// of decoding ones), does best with 5 of 8 (measured on MI355X, same box:
-// decode step 882.9 -> 878.2 us, gate/up back to back 5.34 -> 5.25 us; 3 and
-// 6 of 8, and 3 of 4, were slower).
-template <int R>
-constexpr int kRowWindowF16 = R >= 8 ? 5 : kRowWindow<R>;
 
 struct Split {
   int C;  // chunk-waves per row group
@@ -422,7 +416,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // indices, so every wave streams one contiguous run of rows as in the plain
 // matvec, and the pairs meet in LDS (measured on MI355X, 2 x 16384x4096:
 // 9.7 us with four gate and four up rows per wave).
-template <int R, int CT, int MAXT, int EPI = kStoreF32>
+template <int R, int CT, int MAXT, int EPI = kStoreF32, bool EAGER = true>
 __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
                                                    const uint16_t* __restrict__ x,
                                                    float* __restrict__ y, Split sp) {
@@ -433,14 +427,18 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   uint4* sink = reinterpret_cast<uint4*>(gsum + C * 64);        // [3]
   float* red = reinterpret_cast<float*>(sink + 3);              // [C*S][R]
 
-  // issue priority: 2 while the wave stages x and requests its first rows
-  // (a wave that is starting gets its requests out ahead of waves that are
-  // decoding), 0 while it decodes with rows in flight, 1 once its last row
-  // is requested.  Measured on MI355X, each time both builds on one box:
-  // the start priority took the decode step 905-911 -> 884-886 us and the
-  // gate/up launches back to back 5.55 -> 5.34 us; the tail priority alone
-  // took the step 911-915 -> 904-908 us (single-shape calls unchanged).
-  __builtin_amdgcn_s_setprio(2);
+  // issue priority: with EAGER, 2 while the wave stages x and requests its
+  // first rows (a wave that is starting gets its requests out ahead of waves
+  // that are decoding), then 0 while it decodes with rows in flight; always
+  // 1 once its last row is requested.  Measured on MI355X, each time both
+  // builds on one box: the start priority took the decode step 905-911 ->
+  // 884-886 us and the gate/up launches back to back 5.55 -> 5.34 us, but
+  // the fused gate+up call (1024 workgroups, twice the CUs' two) 8.95 ->
+  // 9.21 us, so the launcher takes EAGER only for grids of at most two
+  // workgroups per CU.  (A run-time flag read from the kernel arguments
+  // lost most of the step gain.)  The tail priority alone took the step
+  // 911-915 -> 904-908 us and left single calls unchanged.
+  if constexpr (EAGER) __builtin_amdgcn_s_setprio(2);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave-uniform indices, kept in scalar registers
@@ -482,9 +480,9 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   constexpr bool PAIR = EPI == kSiluMul;
   uint4 w[R];
   uint16_t hs[R];
-  load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindowF16<R>);
+  load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindow<R>);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(0);
+  if constexpr (EAGER) __builtin_amdgcn_s_setprio(0);
 
   // (2) stage: group m covers weights 16m..16m+15 = group (m % 4) of lane
   //     (m / 4) % 64 of chunk m / 256.  Its 8 operand pairs go to slots
@@ -541,12 +539,12 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r + kRowWindowF16<R> < R) {  // the next row into the window
+    if (r + kRowWindow<R> < R) {  // the next row into the window
       __builtin_amdgcn_sched_barrier(0);
-      load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindowF16<R>, r + kRowWindowF16<R> + 1);
+      load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindow<R>, r + kRowWindow<R> + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (r == R - kRowWindowF16<R>) __builtin_amdgcn_s_setprio(1);  // only decoding is left
+    if (r == R - kRowWindow<R>) __builtin_amdgcn_s_setprio(1);  // only decoding is left
     const uint32_t keep = row_valid<R, PAIR>(ms, row0, r) ? 0xFFFFu : 0u;
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hs[r] & keep));
     acc[r] = __builtin_fmaf((float)d, lane_dot_f16(w[r], xp, seed), 0.0f);  // v_fma_mix
@@ -654,6 +652,28 @@ static hipError_t set_lds_cap(const void* fn) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
+// Launch one instantiation of the fp16 matvec (EAGER: see k_gemv_f16).
+template <int R, int EPI, bool EAGER>
+static hipError_t launch_f16_kernel(const Split& sp, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                                    const MatSet& m, int64_t K, const uint16_t* x, float* y) {
+  if (sp.C == 1) {
+    hipLaunchKernelGGL((k_gemv_f16<R, 1, 512, EPI, EAGER>), grid, block, lds, s, m, K, x, y, sp);
+  } else if (sp.C == 2) {
+    hipLaunchKernelGGL((k_gemv_f16<R, 2, 512, EPI, EAGER>), grid, block, lds, s, m, K, x, y, sp);
+  } else if (sp.C == 4) {
+    hipLaunchKernelGGL((k_gemv_f16<R, 4, 1024, EPI, EAGER>), grid, block, lds, s, m, K, x, y, sp);
+  } else if (block.x <= 512) {
+    hipLaunchKernelGGL((k_gemv_f16<R, 0, 512, EPI, EAGER>), grid, block, lds, s, m, K, x, y, sp);
+  } else {
+    if (lds > 64 * 1024) {
+      const hipError_t e = set_lds_cap(reinterpret_cast<const void*>(&k_gemv_f16<R, 0, 1024, EPI, EAGER>));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_gemv_f16<R, 0, 1024, EPI, EAGER>), grid, block, lds, s, m, K, x, y, sp);
+  }
+  return hipGetLastError();
+}
+
 template <int R, int EPI>
 static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float* y,
                                hipStream_t s) {
@@ -664,28 +684,16 @@ static hipError_t run_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, fl
   const int64_t nwg = EPI == kSiluMulSlots ? (m.row_begin[1] + (int64_t)(sp.S / 2) * R - 1) / ((int64_t)(sp.S / 2) * R)
                                            : (groups + sp.S - 1) / sp.S;
   if (EPI == kSiluMulSlots && sp.S % 2 != 0) return hipErrorInvalidConfiguration;
+  const bool eager = nwg <= 2LL * device_cus();
   const dim3 grid((unsigned)nwg);
   const size_t lds = f16_lds_bytes(sp.C, sp.S, R);
   const dim3 block(64 * sp.C * sp.S);
   const int ct = sp.C <= 4 && sp.C != 3 ? sp.C : 0;
   if ((int64_t)f16_stage_passes(ct) * block.x < (int64_t)sp.C * 256) return hipErrorInvalidConfiguration;
-  if (sp.C == 1) {
-    hipLaunchKernelGGL((k_gemv_f16<R, 1, 512, EPI>), grid, block, lds, s, m, K, x, y, sp);
-  } else if (sp.C == 2) {
-    hipLaunchKernelGGL((k_gemv_f16<R, 2, 512, EPI>), grid, block, lds, s, m, K, x, y, sp);
-  } else if (sp.C == 4) {
-    hipLaunchKernelGGL((k_gemv_f16<R, 4, 1024, EPI>), grid, block, lds, s, m, K, x, y, sp);
-  } else if (block.x <= 512) {
-    hipLaunchKernelGGL((k_gemv_f16<R, 0, 512, EPI>), grid, block, lds, s, m, K, x, y, sp);
-  } else {
-    if (lds > 64 * 1024) {
-      const hipError_t e = set_lds_cap(reinterpret_cast<const void*>(&k_gemv_f16<R, 0, 1024, EPI>));
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((k_gemv_f16<R, 0, 1024, EPI>), grid, block, lds, s, m, K, x, y, sp);
-  }
-  return hipGetLastError();
+  if (eager) return launch_f16_kernel<R, EPI, true>(sp, grid, block, lds, s, m, K, x, y);
+  return launch_f16_kernel<R, EPI, false>(sp, grid, block, lds, s, m, K, x, y);
 }
+
 
 static int f16_waves_per_cu(int64_t K) { return chunks_of(K) == 1 ? 8 : 16; }
 
