@@ -31,9 +31,13 @@ _LIB = None
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        lib = ctypes.CDLL(_build.LIB)
+        # TQ2_ORACLE_SANITIZED=1 loads the AddressSanitizer/UBSan build
+        # (the process must preload the sanitizer runtime)
+        san = os.environ.get("TQ2_ORACLE_SANITIZED") == "1"
+        path = _build.SAN_LIB if san else _build.LIB
+        if not os.path.exists(path):
+            _build.build(sanitize=san)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         lib.oracle_half_to_float.argtypes = [ctypes.c_uint16]

@@ -1243,7 +1243,10 @@ __device__ __forceinline__ int64_t scaled_partial(uint16_t h, int P) {
   const int P24 = (int)((uint32_t)P << 8) >> 8;
   int t = m * P24;
   if (h & 0x8000) t = -t;
-  return (int64_t)t << sh;
+  // times 2^sh as a multiply (a left shift of a negative value is undefined
+  // in C++17); |t| 2^sh < 2^40, so it cannot overflow, and it compiles to
+  // the same 64-bit shift
+  return (int64_t)t * ((int64_t)1 << sh);
 }
 
 // ---- the same transposed reduction for exact int64 sums ----

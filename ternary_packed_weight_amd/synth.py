@@ -92,3 +92,17 @@ def torch_activations(seed: int, K: int, device="cuda"):
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return torch.randn(K, dtype=torch.float32, device=device, generator=g).to(torch.float16)
+
+
+def torch_add_outliers(seed: int, x, frac=0.001, factor=50.0):
+    """Scale round(frac*K) distinct positions of x (drawn with torch's
+    generator seeded by `seed`, on x's device) by `factor` in fp32, then
+    round to fp16: the device form of add_outliers."""
+    import torch
+    g = torch.Generator(device=x.device)
+    g.manual_seed(seed)
+    n_out = int(round(frac * x.numel()))
+    idx = torch.randperm(x.numel(), generator=g, device=x.device)[:n_out]
+    x = x.clone()
+    x[idx] = (x[idx].float() * factor).to(torch.float16)
+    return x

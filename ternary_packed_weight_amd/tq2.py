@@ -98,10 +98,43 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _dev(t, name):
-    if t is None or not t.is_cuda or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous device tensor")
+_F16_BITS = (torch.float16, torch.int16) + ((torch.uint16,) if hasattr(torch, "uint16") else ())
+_DTYPE_NAMES = {torch.uint8: "uint8", torch.int8: "int8", torch.int32: "int32", torch.float32: "float32"}
+
+
+def _dev(t, name, dtypes=None, numel=None, at_least=False):
+    """Check a tensor argument's layout before anything reaches the library:
+    dtype (binary16 data may be float16 or 16-bit integer bit patterns),
+    element count (exact, or a minimum for workspaces) and contiguity.  The
+    C ABI sees pointers only, so a short or mistyped buffer would otherwise
+    be read or written past its end.  Where the tensors live is checked last,
+    for all of a call's tensors at once (_placed)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        want = "/".join(_DTYPE_NAMES.get(d, str(d).replace("torch.", "")) for d in dtypes)
+        raise ValueError(f"{name} must have dtype {want}, got {t.dtype}")
+    if numel is not None:
+        n = t.numel()
+        if (n < numel) if at_least else (n != numel):
+            rel = "at least " if at_least else ""
+            raise ValueError(f"{name} must hold {rel}{numel} elements, got {n}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _placed(**named):
+    """Every tensor of the call is on the GPU, and all on one device."""
+    devs = set()
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"all tensors of a call must be on one device, got {sorted(map(str, devs))}")
 
 
 def tq2_abi_version():
@@ -125,24 +158,54 @@ def tq2_workspace_bytes(op, N, K):
 
 
 def _shape(codes, scales):
-    _dev(codes, "codes")
-    _dev(scales, "scales")
-    N = codes.shape[0]
-    K = codes.shape[-1] * 4 if codes.dim() == 2 else None
-    if K is None or scales.numel() != N * (K // 256):
-        raise ValueError("codes must be [N][K/4] uint8 and scales [N][K/256] fp16 bits")
+    """(N, K) of a packed weight: codes uint8 [N][K/4], scales binary16 with
+    N*K/256 elements."""
+    if not isinstance(codes, torch.Tensor) or codes.dim() != 2:
+        raise ValueError("codes must be a 2-D [N][K/4] uint8 tensor")
+    N, K = codes.shape[0], codes.shape[1] * 4
+    _dev(codes, "codes", (torch.uint8,))
+    if K % 256:
+        raise ValueError(f"codes must be [N][K/4] with K a multiple of 256, got K = {K}")
+    _dev(scales, "scales", _F16_BITS, N * (K // 256))
     return N, K
 
 
+def _ws(ws):
+    if ws is not None:
+        _dev(ws, "ws")
+    return ws
+
+
+def _mat_tensors(mats):
+    out = {}
+    for i, (c, s) in enumerate(mats):
+        out[f"codes[{i}]"], out[f"scales[{i}]"] = c, s
+    return out
+
+
+def _wsb(ws):
+    if ws is None:
+        return 0
+    return ws.numel() * ws.element_size()
+
+
 def tq2_pack(W, codes=None, scales=None, bad_blocks=None, stream=None):
-    _dev(W, "W")
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("W must be a 2-D [N][K] float32 tensor")
     N, K = W.shape
+    _dev(W, "W", (torch.float32,))
+    if K % 256:
+        raise ValueError(f"K must be a multiple of 256, got {K}")
     if codes is None:
         codes = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
     if scales is None:
         scales = torch.empty((N, K // 256), dtype=torch.float16, device=W.device)
     if bad_blocks is None:
         bad_blocks = torch.empty(1, dtype=torch.int32, device=W.device)
+    _dev(codes, "codes", (torch.uint8,), N * (K // 4))
+    _dev(scales, "scales", _F16_BITS, N * (K // 256))
+    _dev(bad_blocks, "bad_blocks", (torch.int32,), 1, at_least=True)
+    _placed(W=W, codes=codes, scales=scales, bad_blocks=bad_blocks)
     _check("tq2_pack", _lib.tq2_pack(_ptr(W), N, K, _ptr(codes), _ptr(scales), _ptr(bad_blocks),
                                      _stream(stream)))
     return codes, scales, bad_blocks
@@ -152,18 +215,26 @@ def tq2_dequant(codes, scales, W=None, stream=None):
     N, K = _shape(codes, scales)
     if W is None:
         W = torch.empty((N, K), dtype=torch.float32, device=codes.device)
+    _dev(W, "W", (torch.float32,), N * K)
+    _placed(codes=codes, scales=scales, W=W)
     _check("tq2_dequant", _lib.tq2_dequant(_ptr(codes), _ptr(scales), N, K, _ptr(W), _stream(stream)))
     return W
 
 
+def _out(t, name, numel, dtype, device):
+    """An output buffer: allocated when not given, else checked."""
+    if t is None:
+        return torch.empty(numel, dtype=dtype, device=device)
+    return _dev(t, name, (dtype,), numel)
+
+
 def tq2_gemv(codes, scales, x, y=None, ws=None, stream=None):
     N, K = _shape(codes, scales)
-    _dev(x, "x")
-    if y is None:
-        y = torch.empty(N, dtype=torch.float32, device=codes.device)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _dev(x, "x", _F16_BITS, K)
+    y = _out(y, "y", N, torch.float32, codes.device)
+    _placed(codes=codes, scales=scales, x=x, y=y, ws=_ws(ws))
     _check("tq2_gemv", _lib.tq2_gemv(_ptr(codes), _ptr(scales), N, K, _ptr(x), _ptr(y), _ptr(ws),
-                                     wsb, _stream(stream)))
+                                     _wsb(ws), _stream(stream)))
     return y
 
 
@@ -171,21 +242,20 @@ def tq2_gemv_gate_up(codes_g, scales_g, codes_u, scales_u, x, y=None, ws=None, s
     N, K = _shape(codes_g, scales_g)
     if _shape(codes_u, scales_u) != (N, K):
         raise ValueError("gate and up must have the same shape")
-    _dev(x, "x")
-    if y is None:
-        y = torch.empty((2, N), dtype=torch.float32, device=codes_g.device)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _dev(x, "x", _F16_BITS, K)
+    y = _out(y, "y", 2 * N, torch.float32, codes_g.device)
+    _placed(codes_g=codes_g, scales_g=scales_g, codes_u=codes_u, scales_u=scales_u, x=x, y=y, ws=_ws(ws))
     _check("tq2_gemv_gate_up", _lib.tq2_gemv_gate_up(
         _ptr(codes_g), _ptr(scales_g), _ptr(codes_u), _ptr(scales_u), N, K, _ptr(x), _ptr(y),
-        _ptr(ws), wsb, _stream(stream)))
-    return y
+        _ptr(ws), _wsb(ws), _stream(stream)))
+    return y.view(2, N)
 
 
 def tq2_quantize_i8(x, s, x_q=None, stream=None):
-    _dev(x, "x")
+    _dev(x, "x", _F16_BITS)
     K = x.numel()
-    if x_q is None:
-        x_q = torch.empty(K, dtype=torch.int8, device=x.device)
+    x_q = _out(x_q, "x_q", K, torch.int8, x.device)
+    _placed(x=x, x_q=x_q)
     _check("tq2_quantize_i8", _lib.tq2_quantize_i8(_ptr(x), K, float(s), _ptr(x_q), _stream(stream)))
     return x_q
 
@@ -194,16 +264,17 @@ def _workspace(op, N, K, ws, device):
     need = tq2_workspace_bytes(op, N, K)
     if ws is None and need not in (0, 2 ** 64 - 1):
         ws = torch.empty(need, dtype=torch.uint8, device=device)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    return ws, wsb
+    return ws, _wsb(ws)
 
 
 def tq2_gemv_i8q(codes, scales, x_q, s, y=None, partials=None, ws=None, stream=None):
     N, K = _shape(codes, scales)
-    _dev(x_q, "x_q")
-    if y is None:
-        y = torch.empty(N, dtype=torch.float32, device=codes.device)
+    _dev(x_q, "x_q", (torch.int8,), K)
+    y = _out(y, "y", N, torch.float32, codes.device)
+    if partials is not None:
+        _dev(partials, "partials", (torch.int32,), N * (K // 256))
     ws, wsb = _workspace(TQ2_OP_GEMV_I8Q, N, K, ws, codes.device)
+    _placed(codes=codes, scales=scales, x_q=x_q, y=y, partials=partials, ws=_ws(ws))
     _check("tq2_gemv_i8q", _lib.tq2_gemv_i8q(_ptr(codes), _ptr(scales), N, K, _ptr(x_q), float(s),
                                              _ptr(y), _ptr(partials), _ptr(ws), wsb, _stream(stream)))
     return y
@@ -211,10 +282,10 @@ def tq2_gemv_i8q(codes, scales, x_q, s, y=None, partials=None, ws=None, stream=N
 
 def tq2_gemv_i8(codes, scales, x, s, y=None, ws=None, stream=None):
     N, K = _shape(codes, scales)
-    _dev(x, "x")
-    if y is None:
-        y = torch.empty(N, dtype=torch.float32, device=codes.device)
+    _dev(x, "x", _F16_BITS, K)
+    y = _out(y, "y", N, torch.float32, codes.device)
     ws, wsb = _workspace(TQ2_OP_GEMV_I8, N, K, ws, codes.device)
+    _placed(codes=codes, scales=scales, x=x, y=y, ws=_ws(ws))
     _check("tq2_gemv_i8", _lib.tq2_gemv_i8(_ptr(codes), _ptr(scales), N, K, _ptr(x), float(s),
                                            _ptr(y), _ptr(ws), wsb, _stream(stream)))
     return y
@@ -239,23 +310,21 @@ def _host_arrays(mats):
 def tq2_gemv_fused(mats, x, y=None, ws=None, stream=None):
     """y = concatenation of W_i x over mats = [(codes_i, scales_i), ...]."""
     n, cp, sp, Np, Ns, K = _host_arrays(mats)
-    _dev(x, "x")
-    if y is None:
-        y = torch.empty(sum(Ns), dtype=torch.float32, device=x.device)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check("tq2_gemv_fused", _lib.tq2_gemv_fused(n, cp, sp, Np, K, _ptr(x), _ptr(y), _ptr(ws), wsb,
+    _dev(x, "x", _F16_BITS, K)
+    y = _out(y, "y", sum(Ns), torch.float32, x.device)
+    _placed(x=x, y=y, ws=_ws(ws), **_mat_tensors(mats))
+    _check("tq2_gemv_fused", _lib.tq2_gemv_fused(n, cp, sp, Np, K, _ptr(x), _ptr(y), _ptr(ws), _wsb(ws),
                                                  _stream(stream)))
     return y
 
 
 def tq2_gemv_i8_fused(mats, x, s, y=None, ws=None, stream=None):
     n, cp, sp, Np, Ns, K = _host_arrays(mats)
-    _dev(x, "x")
-    if y is None:
-        y = torch.empty(sum(Ns), dtype=torch.float32, device=x.device)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _dev(x, "x", _F16_BITS, K)
+    y = _out(y, "y", sum(Ns), torch.float32, x.device)
+    _placed(x=x, y=y, ws=_ws(ws), **_mat_tensors(mats))
     _check("tq2_gemv_i8_fused", _lib.tq2_gemv_i8_fused(n, cp, sp, Np, K, _ptr(x), float(s), _ptr(y),
-                                                       _ptr(ws), wsb, _stream(stream)))
+                                                       _ptr(ws), _wsb(ws), _stream(stream)))
     return y
 
 
@@ -263,28 +332,26 @@ def tq2_gemv_gate_up_silu(codes_g, scales_g, codes_u, scales_u, x, h=None, ws=No
     N, K = _shape(codes_g, scales_g)
     if _shape(codes_u, scales_u) != (N, K):
         raise ValueError("gate and up must have the same shape")
-    _dev(x, "x")
-    if h is None:
-        h = torch.empty(N, dtype=torch.float32, device=codes_g.device)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _dev(x, "x", _F16_BITS, K)
+    h = _out(h, "h", N, torch.float32, codes_g.device)
+    _placed(codes_g=codes_g, scales_g=scales_g, codes_u=codes_u, scales_u=scales_u, x=x, h=h, ws=_ws(ws))
     _check("tq2_gemv_gate_up_silu", _lib.tq2_gemv_gate_up_silu(
         _ptr(codes_g), _ptr(scales_g), _ptr(codes_u), _ptr(scales_u), N, K, _ptr(x), _ptr(h),
-        _ptr(ws), wsb, _stream(stream)))
+        _ptr(ws), _wsb(ws), _stream(stream)))
     return h
 
 
 def tq2_gemv_i8_requant(codes, scales, x, s_in, s_out, y_q=None, y_deq=None, want_deq=True,
                         ws=None, stream=None):
     N, K = _shape(codes, scales)
-    _dev(x, "x")
-    if y_q is None:
-        y_q = torch.empty(N, dtype=torch.int8, device=codes.device)
-    if y_deq is None and want_deq:
-        y_deq = torch.empty(N, dtype=torch.float32, device=codes.device)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _dev(x, "x", _F16_BITS, K)
+    y_q = _out(y_q, "y_q", N, torch.int8, codes.device)
+    if y_deq is not None or want_deq:
+        y_deq = _out(y_deq, "y_deq", N, torch.float32, codes.device)
+    _placed(codes=codes, scales=scales, x=x, y_q=y_q, y_deq=y_deq, ws=_ws(ws))
     _check("tq2_gemv_i8_requant", _lib.tq2_gemv_i8_requant(
         _ptr(codes), _ptr(scales), N, K, _ptr(x), float(s_in), float(s_out), _ptr(y_q), _ptr(y_deq),
-        _ptr(ws), wsb, _stream(stream)))
+        _ptr(ws), _wsb(ws), _stream(stream)))
     return y_q, y_deq
 
 
@@ -296,16 +363,17 @@ def tq2_gemm(codes, scales, x, y=None, ws=None, stream=None):
     """Y[M][N] = X[M][K] W^T for x of shape [M, K] (fp16); allocates the
     workspace when none is given."""
     N, K = _shape(codes, scales)
-    _dev(x, "x")
-    if x.dim() != 2 or x.shape[1] != K:
-        raise ValueError(f"x must be [M, {K}]")
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be a [M, {K}] tensor")
     M = x.shape[0]
-    if y is None:
-        y = torch.empty(M, N, dtype=torch.float32, device=codes.device)
+    _dev(x, "x", _F16_BITS, M * K)
+    y = _out(y, "y", M * N, torch.float32, codes.device)
     need = tq2_gemm_workspace_bytes(N, K, M)
-    if ws is None and need:
+    if ws is None and need and need != 2 ** 64 - 1:
         ws = torch.empty(need, dtype=torch.uint8, device=codes.device)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check("tq2_gemm", _lib.tq2_gemm(_ptr(codes), _ptr(scales), N, K, _ptr(x), M, _ptr(y), _ptr(ws), wsb,
+    if ws is not None and need and need != 2 ** 64 - 1:
+        _dev(ws, "ws", None, need // ws.element_size(), at_least=True)
+    _placed(codes=codes, scales=scales, x=x, y=y, ws=ws)
+    _check("tq2_gemm", _lib.tq2_gemm(_ptr(codes), _ptr(scales), N, K, _ptr(x), M, _ptr(y), _ptr(ws), _wsb(ws),
                                       _stream(stream)))
-    return y
+    return y.view(M, N)

@@ -55,3 +55,46 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one MI355X" in r.stderr
+
+
+def test_every_configuration_rotates_past_the_infinity_cache():
+    # one graph touches every copy once, and the copies total >= 1.1 GB, so
+    # no timed call finds its weights in the 256 MB Infinity Cache
+    for label, N, K, kind, seed in bench.CONFIGS:
+        rows = bench.QKV_ROWS if kind in ("qkv", "qkv_i8") else ((N, N) if kind in ("gate_up", "silu") else (N,))
+        nbytes = bench.config_bytes(kind, N, K, rows)
+        ncopy, ncall = bench.rotation(nbytes, None)
+        assert ncall == ncopy and ncall * nbytes >= bench.ROTATION_BYTES, label
+    assert bench.config_bytes("gate_up", 16384, 4096, (16384, 16384)) == 34_742_272
+    assert bench.config_bytes("i8", 4096, 16384, (4096,)) == 17_350_656
+    assert bench.config_bytes("f16", 256, 4096, (256,)) == 279_552
+
+
+def test_trace_summary_splits_sections_at_markers(tmp_path, monkeypatch):
+    """A synthetic rocprofv3 kernel trace: dispatches are assigned to the
+    section of the last marker kernel before them (by start time), and the
+    record carries the kernel source of the traced run."""
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    hdr = ("Kind,Agent_Id,Queue_Id,Kernel_Name,Start_Timestamp,End_Timestamp,"
+           "Workgroup_Size_X,Grid_Size_X\n")
+    rows = [("(anonymous namespace)::k_empty()", 100, 101, 64, 64 * bench.MARK_DOMINANT),
+            ("tq2::k_gemv_f16<8, 1, 512, 0, true>", 200, 5200, 256, 131072),
+            ("tq2::k_gemv_f16<8, 1, 512, 0, true>", 6000, 12000, 256, 131072),
+            ("(anonymous namespace)::k_empty()", 13000, 13001, 64, 64 * (bench.MARK_CONFIG + 4)),
+            ("tq2::k_gemv_i8<4, true, false, 4, 1024, false>", 14000, 20000, 1024, 262144)]
+    csv = tmp_path / "run_kernel_trace.csv"
+    csv.write_text(hdr + "".join(f"KERNEL_DISPATCH,1,1,\"{n}\",{s},{e},{w},{g}\n" for n, s, e, w, g in rows))
+    line = {"trace_markers": {str(bench.MARK_DOMINANT): "dominant kernel",
+                              str(bench.MARK_CONFIG + 4): bench.CONFIGS[4][0]},
+            "provenance": {"kernel_source_sha": "abc", "source_sha": "def",
+                           "gpu": {"name": "x", "arch": "gfx950"}}}
+    js = tmp_path / "b.json"
+    js.write_text("log line\n" + json.dumps(line) + "\n")
+    bench.trace_summary(str(tmp_path), str(js), "rocprofv3 ...")
+    rec = json.loads((tmp_path / "profiles" / bench.TRACE_FILE).read_text())
+    assert rec["kernel_source_sha"] == "abc"
+    dom = rec["sections"]["dominant kernel"][0]
+    assert dom["dispatches"] == 2 and dom["mean_us"] == 5.5 and dom["grid_threads"] == 131072
+    assert bench.trace_kernel_us(rec, bench.CONFIGS[4][0]) == (6.0, rows[4][0])
+    assert bench.trace_kernel_us(rec, "decode step") == (None, None)
