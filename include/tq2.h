@@ -20,7 +20,9 @@
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers that the caller allocates, owns
  *     and keeps alive until the work completes.  The library allocates
- *     nothing and keeps no mutable state; calls are thread-safe.
+ *     nothing and keeps no mutable state; calls are thread-safe.  (One
+ *     exception: tq2_gemm_noalloc keeps its split partials in a static
+ *     device array per GPU; see there.)
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *     default stream) and returns; results are valid once the caller has
  *     synchronized the stream.  Nothing synchronizes inside.
@@ -56,7 +58,8 @@ enum tq2_status {
     TQ2_ERR_ALIGN = 3,     /* a pointer violates its alignment             */
     TQ2_ERR_WORKSPACE = 4, /* workspace missing or smaller than required   */
     TQ2_ERR_SCALE = 5,     /* int8 activation scale not finite or <= 0     */
-    TQ2_ERR_HIP = 6        /* the HIP runtime refused a launch             */
+    TQ2_ERR_HIP = 6,       /* the HIP runtime refused a launch             */
+    TQ2_ERR_SCRATCH = 7    /* more scratch than tq2_gemm_noalloc holds     */
 };
 
 enum tq2_op {
@@ -226,6 +229,25 @@ size_t tq2_gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);
 int32_t tq2_gemm(const uint8_t *codes, const uint16_t *scales, int64_t N,
                  int64_t K, const uint16_t *x, int64_t M, float *y, void *ws,
                  size_t ws_bytes, tq2_stream_t stream);
+
+/* tq2_gemm_noalloc -- tq2_gemm for callers that cannot allocate (code
+ * under HIP graph capture, serving loops or harnesses that forbid
+ * hipMalloc): the same kernels and results (bit-identical to tq2_gemm), but
+ * the split partials live in a static device array of the library,
+ * TQ2_GEMM_SCRATCH_BYTES per GPU, held by every GPU the library runs on
+ * until the process ends.  Allocates nothing (no hipMalloc, no allocating
+ * library routine).  Returns TQ2_ERR_SCRATCH, before any launch, when
+ * tq2_gemm_workspace_bytes(N, K, M) exceeds TQ2_GEMM_SCRATCH_BYTES (on
+ * MI355X no shape needs more than 2 MiB).  The first call on a device looks
+ * the array's device address up (hipGetSymbolAddress) on the device of
+ * `stream`.  All calls on one GPU share its array and every call overwrites
+ * what it uses: calls that can overlap on one GPU (concurrent streams, or
+ * other host threads) race and must be serialized by the caller.  Nothing in
+ * the array needs to start at zero. */
+#define TQ2_GEMM_SCRATCH_BYTES 4194304
+int32_t tq2_gemm_noalloc(const uint8_t *codes, const uint16_t *scales,
+                         int64_t N, int64_t K, const uint16_t *x, int64_t M,
+                         float *y, tq2_stream_t stream);
 
 #ifdef __cplusplus
 }

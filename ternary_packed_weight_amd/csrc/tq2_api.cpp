@@ -57,6 +57,7 @@ const char* tq2_status_string(int32_t status) {
     case TQ2_ERR_WORKSPACE: return "workspace missing or too small";
     case TQ2_ERR_SCALE: return "activation scale must be finite and > 0";
     case TQ2_ERR_HIP: return "HIP launch failed";
+    case TQ2_ERR_SCRATCH: return "split partials exceed the library's static scratch (TQ2_GEMM_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -286,22 +287,51 @@ size_t tq2_gemm_workspace_bytes(int64_t N, int64_t K, int64_t M) {
   return tq2::gemm_workspace_bytes(N, K, M);
 }
 
-int32_t tq2_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const uint16_t* x,
-                 int64_t M, float* y, void* ws, size_t ws_bytes, tq2_stream_t stream) {
+}  // extern "C"
+
+// tq2_gemm's checks of everything but the workspace.
+static int32_t gemm_args(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                         const uint16_t* x, int64_t M, float* y) {
   TQ2_TRY(check_shape(N, K, TQ2_MAX_K));
   TQ2_TRY(check_weights(codes, scales));
   if (M < 1 || M > TQ2_MAX_TOKENS || !x || !y) return TQ2_ERR_ARG;
   if (M * N > ((int64_t)1 << 40)) return TQ2_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, 4)) return TQ2_ERR_ALIGN;
-  const size_t need = tq2::gemm_workspace_bytes(N, K, M);
-  if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return TQ2_ERR_WORKSPACE;
   const size_t xb = (size_t)(M * K) * 2, yb = (size_t)(M * N) * 4;
   const size_t cb = (size_t)(N * (K / 4)), sb = (size_t)(N * (K / TQ2_BLOCK)) * 2;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, codes, cb) || overlaps(y, yb, scales, sb))
     return TQ2_ERR_ARG;
+  return TQ2_OK;
+}
+
+static_assert(TQ2_GEMM_SCRATCH_BYTES == tq2::kGemmScratchBytes, "scratch size of the header and the library");
+
+extern "C" {
+
+int32_t tq2_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const uint16_t* x,
+                 int64_t M, float* y, void* ws, size_t ws_bytes, tq2_stream_t stream) {
+  TQ2_TRY(gemm_args(codes, scales, N, K, x, M, y));
+  const size_t need = tq2::gemm_workspace_bytes(N, K, M);
+  if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return TQ2_ERR_WORKSPACE;
+  const size_t xb = (size_t)(M * K) * 2, yb = (size_t)(M * N) * 4;
+  const size_t cb = (size_t)(N * (K / 4)), sb = (size_t)(N * (K / TQ2_BLOCK)) * 2;
   if (need && (overlaps(ws, need, x, xb) || overlaps(ws, need, y, yb) || overlaps(ws, need, codes, cb) ||
                overlaps(ws, need, scales, sb)))
     return TQ2_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return hip_status(tq2::launch_gemm(codes, scales, N, K, x, M, y, ws, (hipStream_t)stream));
+}
+
+int32_t tq2_gemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                         const uint16_t* x, int64_t M, float* y, tq2_stream_t stream) {
+  TQ2_TRY(gemm_args(codes, scales, N, K, x, M, y));
+  const size_t need = tq2::gemm_workspace_bytes(N, K, M);
+  if (need > TQ2_GEMM_SCRATCH_BYTES) return TQ2_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need) {
+    (void)hipGetLastError();
+    if (tq2::gemm_scratch((hipStream_t)stream, &ws) != hipSuccess) return TQ2_ERR_HIP;
+  }
   (void)hipGetLastError();
   return hip_status(tq2::launch_gemm(codes, scales, N, K, x, M, y, ws, (hipStream_t)stream));
 }

@@ -64,4 +64,10 @@ size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);
 hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                        const uint16_t* x, int64_t M, float* y, void* ws, hipStream_t st);
 
+// Device address of the library's static scratch array (kGemmScratchBytes,
+// 256-byte aligned) on the device of `st` (the current device when st is
+// null), looked up with hipGetSymbolAddress on first use per device.
+constexpr size_t kGemmScratchBytes = (size_t)4 << 20;
+hipError_t gemm_scratch(hipStream_t st, void** out);
+
 }  // namespace tq2

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tq2_internal.h"
 
 namespace tq2 {
@@ -1586,6 +1588,47 @@ hipError_t launch_gemv_i8_requant(const MatSet& m, int64_t K, const uint16_t* x,
     case 4: return run_gemv_i8_r<4>(m, K, x, nullptr, s, nullptr, nullptr, &rq, st);
     default: return run_gemv_i8_r<2>(m, K, x, nullptr, s, nullptr, nullptr, &rq, st);
   }
+}
+
+// ------------------------------------------- static scratch (no allocation)
+// For callers that cannot allocate (graph capture, serving loops that forbid
+// hipMalloc): tq2_gemm's split partials live in this file-scope device array
+// instead of a caller workspace.  Every GPU the library runs on holds its own
+// copy, at its own address, until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory, so its device address is
+// taken once per device with hipGetSymbolAddress (that device current) and
+// only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[kGemmScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t gemm_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace tq2

@@ -63,13 +63,18 @@ _lib.tq2_gemm_workspace_bytes.argtypes = [_I64, _I64, _I64]
 _lib.tq2_gemm_workspace_bytes.restype = _SZ
 _lib.tq2_gemm.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]
 _lib.tq2_gemm.restype = _I32
+_lib.tq2_gemm_noalloc.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P]
+_lib.tq2_gemm_noalloc.restype = _I32
 
 TQ2_OK = 0
 TQ2_OP_GEMV, TQ2_OP_GATE_UP, TQ2_OP_GEMV_I8, TQ2_OP_GEMV_I8Q = 0, 1, 2, 3
 EXPORTED = ("tq2_abi_version", "tq2_status_string", "tq2_codes_bytes", "tq2_scales_bytes",
             "tq2_workspace_bytes", "tq2_pack", "tq2_dequant", "tq2_gemv", "tq2_gemv_gate_up",
             "tq2_quantize_i8", "tq2_gemv_i8q", "tq2_gemv_i8", "tq2_gemv_fused", "tq2_gemv_i8_fused",
-            "tq2_gemv_gate_up_silu", "tq2_gemv_i8_requant", "tq2_gemm_workspace_bytes", "tq2_gemm")
+            "tq2_gemv_gate_up_silu", "tq2_gemv_i8_requant", "tq2_gemm_workspace_bytes", "tq2_gemm",
+            "tq2_gemm_noalloc")
+TQ2_ERR_SCRATCH = 7
+TQ2_GEMM_SCRATCH_BYTES = 4194304
 
 
 class Tq2Error(RuntimeError):
@@ -376,4 +381,20 @@ def tq2_gemm(codes, scales, x, y=None, ws=None, stream=None):
     _placed(codes=codes, scales=scales, x=x, y=y, ws=ws)
     _check("tq2_gemm", _lib.tq2_gemm(_ptr(codes), _ptr(scales), N, K, _ptr(x), M, _ptr(y), _ptr(ws), _wsb(ws),
                                       _stream(stream)))
+    return y.view(M, N)
+
+
+def tq2_gemm_noalloc(codes, scales, x, y=None, stream=None):
+    """tq2_gemm with the split partials in the library's static scratch (no
+    workspace argument, nothing allocated by the library; y is allocated
+    here only when not given)."""
+    N, K = _shape(codes, scales)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be a [M, {K}] tensor")
+    M = x.shape[0]
+    _dev(x, "x", _F16_BITS, M * K)
+    y = _out(y, "y", M * N, torch.float32, codes.device)
+    _placed(codes=codes, scales=scales, x=x, y=y)
+    _check("tq2_gemm_noalloc", _lib.tq2_gemm_noalloc(_ptr(codes), _ptr(scales), N, K, _ptr(x), M, _ptr(y),
+                                                      _stream(stream)))
     return y.view(M, N)

@@ -207,3 +207,17 @@ def test_gemm_split_rule(tq2):
     assert ws(4096, 16384, 48) == 2 * 48 * 4096 * 4  # 128 workgroups -> 2 splits
     assert ws(4096, 4096, 16) == 4 * 16 * 4096 * 4   # 64 -> 4 (every wave keeps its step)
     assert ws(4096, 4096, 32) == 2 * 32 * 4096 * 4   # 128 -> 2
+
+
+def test_noalloc_scratch_covers_every_split(tq2):
+    """tq2_gemm_noalloc's static scratch (TQ2_GEMM_SCRATCH_BYTES) holds the
+    split partials of every shape: the plan splits K only while row sets x
+    token groups x splits fit the 256 CUs, which bounds the partials by
+    2 MiB.  Checked over a grid of shapes and token counts."""
+    worst = 0
+    for N in (1, 16, 64, 100, 256, 300, 1000, 1024, 2048, 4096, 8192, 16384):
+        for K in (256, 1024, 4096, 4352, 16384, 65536):
+            for M in (1, 2, 3, 5, 8, 16, 17, 32, 33, 48, 64, 100, 128, 256, 1024):
+                worst = max(worst, tq2.tq2_gemm_workspace_bytes(N, K, M))
+    assert 0 < worst <= 2 << 20 <= tq2.TQ2_GEMM_SCRATCH_BYTES
+    assert "tq2_gemm_noalloc" in declared_functions()
