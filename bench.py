@@ -67,7 +67,7 @@ METRIC = "tq2_gemv achieved HBM GB/s and % of MI355X peak; 224-linear decode ste
 STEP_SEEDS = {"weights": "10000 + 7*layer + proj", "x": "20000 + 7*layer + proj"}
 
 # trace-marker ids (workgroups of the empty marker kernel) of the timed sections
-MARK_STEP, MARK_DOMINANT, MARK_FUSED, MARK_FLOOR, MARK_SWEEP = 1, 2, 3, 4, 5
+MARK_STEP, MARK_DOMINANT, MARK_FUSED, MARK_FLOOR, MARK_SWEEP, MARK_END = 1, 2, 3, 4, 5, 6
 MARK_CONFIG, MARK_CONFIG_PROBE = 100, 200  # + index of the configuration
 
 
@@ -581,6 +581,8 @@ def time_rotating(torch, probes, calls, reps, mark):
     if probes is not None:
         probes.marker(mark)
     ts = [time_graph(torch, g, 1) / len(calls) for _ in range(reps)]
+    if probes is not None:
+        probes.marker(MARK_END)
     del g
     return float(np.median(ts)), float(np.percentile(ts, 95))
 
@@ -660,7 +662,9 @@ def dispatch_floor(torch, probes, n=400, reps=10):
     g = capture(torch, [probes.empty for _ in range(n)])
     time_graph(torch, g, 3)
     probes.marker(MARK_FLOOR)
-    return float(np.median([time_graph(torch, g, 1) / n for _ in range(reps)]))
+    us = float(np.median([time_graph(torch, g, 1) / n for _ in range(reps)]))
+    probes.marker(MARK_END)
+    return us
 
 
 def probe_sweep(torch, probes, reps=5):
@@ -684,6 +688,7 @@ def probe_sweep(torch, probes, reps=5):
             log(f"sweep {nbytes} B {variant_name(v)}: {us:.3f} us, {nbytes / us / 1e3:.1f} GB/s")
         del pool
         torch.cuda.empty_cache()
+    probes.marker(MARK_END)
     return rows
 
 
@@ -713,6 +718,7 @@ def fused_step(torch, tq2, stack, steps, probes):
     time_graph(torch, graph, 20)  # untimed warm-up replays
     probes.marker(MARK_FUSED)
     us = time_graph(torch, graph, steps)
+    probes.marker(MARK_END)
     q, k, v, o, g, u, d = layers[0]
     yqkv, ygu = bufs[0]
     ref = torch.cat([tq2.tq2_gemv(e["codes"], e["scales"], q["x"]) for e in (q, k, v)])
@@ -764,7 +770,7 @@ def trace_summary(trace_path, bench_json_path, command):
     current = None
     for start, end, name, grid, wg in rows:
         if "k_empty" in name and wg == 64 and (grid // 64) in markers:
-            current = markers[grid // 64]
+            current = markers[grid // 64]  # None: the end of a timed section
             continue
         if current is None:
             continue
@@ -858,7 +864,7 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f16", "accumulate": "f32", "data": "synthetic"}
     markers = {MARK_STEP: "decode step", MARK_DOMINANT: "dominant kernel", MARK_FUSED: "step_fused",
-               MARK_FLOOR: "dispatch floor", MARK_SWEEP: "read probe sweep"}
+               MARK_FLOOR: "dispatch floor", MARK_SWEEP: "read probe sweep", MARK_END: None}
     for ci, c in enumerate(CONFIGS):
         markers[MARK_CONFIG + ci] = c[0]
         markers[MARK_CONFIG_PROBE + ci] = "read probe: " + c[0]
@@ -881,6 +887,7 @@ def main():
         probes.marker(MARK_STEP)
         t_start = time.perf_counter()
         us_step = time_graph(torch, step_graph, args.steps)
+        probes.marker(MARK_END)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         step_bytes = sum(algo_bytes(e["N"], e["K"]) for e in stack)
@@ -893,6 +900,7 @@ def main():
         time_graph(torch, dom_graph, 20)  # untimed warm-up replays
         probes.marker(MARK_DOMINANT)
         us_dom = time_graph(torch, dom_graph, max(3, args.steps // 2)) / len(dom)
+        probes.marker(MARK_END)
         dom_bytes = sum(algo_bytes(e["N"], e["K"]) for e in dom) / len(dom)
         achieved = dom_bytes / us_dom / 1e3
         us_tr, kname = trace_kernel_us(trace, markers[MARK_DOMINANT])

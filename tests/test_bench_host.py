@@ -81,11 +81,13 @@ def test_trace_summary_splits_sections_at_markers(tmp_path, monkeypatch):
     rows = [("(anonymous namespace)::k_empty()", 100, 101, 64, 64 * bench.MARK_DOMINANT),
             ("tq2::k_gemv_f16<8, 1, 512, 0, true>", 200, 5200, 256, 131072),
             ("tq2::k_gemv_f16<8, 1, 512, 0, true>", 6000, 12000, 256, 131072),
+            ("(anonymous namespace)::k_empty()", 12100, 12101, 64, 64 * bench.MARK_END),
+            ("tq2::k_gemv_f16<8, 1, 512, 0, true>", 12200, 12300, 256, 131072),   # untimed: ignored
             ("(anonymous namespace)::k_empty()", 13000, 13001, 64, 64 * (bench.MARK_CONFIG + 4)),
             ("tq2::k_gemv_i8<4, true, false, 4, 1024, false>", 14000, 20000, 1024, 262144)]
     csv = tmp_path / "run_kernel_trace.csv"
     csv.write_text(hdr + "".join(f"KERNEL_DISPATCH,1,1,\"{n}\",{s},{e},{w},{g}\n" for n, s, e, w, g in rows))
-    line = {"trace_markers": {str(bench.MARK_DOMINANT): "dominant kernel",
+    line = {"trace_markers": {str(bench.MARK_DOMINANT): "dominant kernel", str(bench.MARK_END): None,
                               str(bench.MARK_CONFIG + 4): bench.CONFIGS[4][0]},
             "provenance": {"kernel_source_sha": "abc", "source_sha": "def",
                            "gpu": {"name": "x", "arch": "gfx950"}}}
@@ -96,5 +98,5 @@ def test_trace_summary_splits_sections_at_markers(tmp_path, monkeypatch):
     assert rec["kernel_source_sha"] == "abc"
     dom = rec["sections"]["dominant kernel"][0]
     assert dom["dispatches"] == 2 and dom["mean_us"] == 5.5 and dom["grid_threads"] == 131072
-    assert bench.trace_kernel_us(rec, bench.CONFIGS[4][0]) == (6.0, rows[4][0])
+    assert bench.trace_kernel_us(rec, bench.CONFIGS[4][0]) == (6.0, rows[6][0])
     assert bench.trace_kernel_us(rec, "decode step") == (None, None)
