@@ -375,12 +375,16 @@ __device__ __forceinline__ void load_rows(const MatSet& ms, int row0, int64_t kk
   }
 }
 
-// Rows a wave keeps in flight.  The first kRowWindow rows are requested at
-// the start; row r + kRowWindow just before row r is decoded.  All R at once
-// let the waves that start first fill the memory queues with all their rows,
-// so the waves dispatched last got all of theirs at the end of the stream and
-// decoded them after it (measured on MI355X: 16384x4096 6.0 -> 5.8 us,
-// 4096x16384 6.45 -> 5.95 us; windows of 2 or 6 of 8 rows were slower).
+// Rows a wave requests before the activations are staged.  The rest follow
+// in one burst as soon as the wave has its activations (before its first
+// decode), not one row per decoded row: x comes from HBM, so the first decode
+// waits ~1.1-1.6 us for it, and by then the first window has mostly arrived;
+// requesting the rest only as rows were decoded left HBM idle in that gap
+// and sent the last rows to the end of the stream (measured on MI355X, both
+// forms on one box: decode step 881 -> 864 us, 16384x4096 5.35 -> 5.21 us,
+// 4096x16384 6.29 -> 5.99 us, the int8 down 6.23 -> 6.12 us).  All R rows at
+// the start is slower again (4096x16384 +0.7 us): the flood of weight
+// requests delays the activations, which come from HBM as well.
 template <int R>
 constexpr int kRowWindow = R >= 8 ? 4 : (R >= 4 ? 2 : R);
 
@@ -429,10 +433,11 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   uint4* sink = reinterpret_cast<uint4*>(gsum + C * 64);        // [3]
   float* red = reinterpret_cast<float*>(sink + 3);              // [C*S][R]
 
-  // issue priority: with EAGER, 2 while the wave stages x and requests its
-  // first rows (a wave that is starting gets its requests out ahead of waves
-  // that are decoding), then 0 while it decodes with rows in flight; always
-  // 1 once its last row is requested.  Measured on MI355X, each time both
+  // issue priority: with EAGER, 2 while the wave requests x and its first
+  // rows (a wave that is starting gets its requests out ahead of waves that
+  // are decoding), then 0 while it waits for x and stages it; always 1 once
+  // its last row is requested (the burst after staging).  Measured on
+  // MI355X, when rows were still requested one per decoded row, each time both
   // builds on one box: the start priority took the decode step 905-911 ->
   // 884-886 us and the gate/up launches back to back 5.55 -> 5.34 us, but
   // the fused gate+up call (1024 workgroups, twice the CUs' two) 8.95 ->
@@ -478,6 +483,14 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
     xa[p] = load_b128(xr, 32 * m);
     xb[p] = load_b128(xr, 32 * m + 16);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // every wave of the workgroup has requested its share of x before any
+  // wave requests weights: a CU returns vector loads in request order across
+  // its waves, so x requested after another wave's rows waited for those
+  // rows to come from HBM (measured on MI355X: 4096x16384 5.93 -> 5.55 us,
+  // int8 down 6.06 -> 5.72 us, decode step 864 -> 852 us).  A bare
+  // s_barrier: no memory wait, the loads stay in flight.
+  __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   constexpr bool PAIR = EPI == kSiluMul;
   uint4 w[R];
@@ -535,18 +548,18 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   }
   const float4 gs = gsum[c * 64 + lane];
   const float seed = -ldexpf((gs.x + gs.y) + (gs.z + gs.w), -24);
+  if constexpr (kRowWindow<R> < R) {  // the rest of the rows, in one burst
+    __builtin_amdgcn_sched_barrier(0);
+    load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, kRowWindow<R>, R);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(1);  // every row is requested: only decoding is left
 
   // lanes past K hold x = 0 and seed 0, so only padding rows need zeroing;
   // the row test is wave-uniform (a scalar select of the mask)
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r + kRowWindow<R> < R) {  // the next row into the window
-      __builtin_amdgcn_sched_barrier(0);
-      load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindow<R>, r + kRowWindow<R> + 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (r == R - kRowWindow<R>) __builtin_amdgcn_s_setprio(1);  // only decoding is left
     const uint32_t keep = row_valid<R, PAIR>(ms, row0, r) ? 0xFFFFu : 0u;
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hs[r] & keep));
     acc[r] = __builtin_fmaf((float)d, lane_dot_f16(w[r], xp, seed), 0.0f);  // v_fma_mix
@@ -1400,6 +1413,8 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();  // x of every wave ahead of any weight request (see k_gemv_f16)
+  __builtin_amdgcn_sched_barrier(0);
   uint4 w[R];
   uint16_t hs[R];
   load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindow<R>);
@@ -1472,15 +1487,15 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
   }
   const int4 gs4 = reinterpret_cast<const int4*>(gsum)[c * 64 + lane];
   const int seed = -((gs4.x + gs4.y) + (gs4.z + gs4.w));
+  if constexpr (kRowWindow<R> < R) {  // the rest of the rows, in one burst
+    __builtin_amdgcn_sched_barrier(0);
+    load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs, kRowWindow<R>, R);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   int64_t acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r + kRowWindow<R> < R) {  // the next row into the window
-      __builtin_amdgcn_sched_barrier(0);
-      load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs, r + kRowWindow<R>, r + kRowWindow<R> + 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
     const int P = lane_dot_i8(w[r], xq, seed);
     const uint32_t keep = (row0 + r < ms.rows ? 0xFFFFu : 0u) & (0u - (uint32_t)active);
     acc[r] = scaled_partial((uint16_t)(hs[r] & keep), P);
