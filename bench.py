@@ -390,7 +390,7 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
 ]
 QKV_ROWS = (4096, 256, 256)
 ROTATION_BYTES = 1.1e9  # > the 256 MB Infinity Cache: every timed call streams from HBM
-WARM_REPLAYS = 3  # untimed graph replays before each configuration's timed ones
+WARM_REPLAYS = 10  # untimed graph replays before each configuration's timed ones (the first replays after setup run slower)
 REQUANT_S_OUT = 0.05
 CPU_TIMED_KINDS = ("f16", "f16_out", "gate_up", "i8", "i8q")
 

@@ -427,6 +427,14 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
                                                    const uint16_t* __restrict__ x,
                                                    float* __restrict__ y, Split sp) {
   extern __shared__ uint4 lds[];
+  // rows requested before x is staged (the rest follow in one burst after
+  // it).  Grids of more than two workgroups per CU (not EAGER) with 8 rows
+  // per wave request 1: a CU returns loads in request order, so a later
+  // workgroup's x waits behind the first windows of the workgroups before it
+  // on the CU (measured on MI355X, same box: fused gate+up 2x16384x4096
+  // 8.47 -> 8.29 us, with SiLU 8.68 -> 8.36 us; a window of 0 was slower
+  // again, and smaller windows for the EAGER grids were slower).
+  constexpr int KW = (EAGER || R < 8) ? kRowWindow<R> : 1;
   const int C = CT ? CT : sp.C, S = sp.S;
   uint4* xpairs = lds;                                          // [C][8][64]
   float4* gsum = reinterpret_cast<float4*>(lds + C * 8 * 64);   // [C][64]
@@ -495,7 +503,7 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   constexpr bool PAIR = EPI == kSiluMul;
   uint4 w[R];
   uint16_t hs[R];
-  load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindow<R>);
+  load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, 0, KW);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (EAGER) __builtin_amdgcn_s_setprio(0);
 
@@ -548,9 +556,9 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   }
   const float4 gs = gsum[c * 64 + lane];
   const float seed = -ldexpf((gs.x + gs.y) + (gs.z + gs.w), -24);
-  if constexpr (kRowWindow<R> < R) {  // the rest of the rows, in one burst
+  if constexpr (KW < R) {  // the rest of the rows, in one burst
     __builtin_amdgcn_sched_barrier(0);
-    load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, kRowWindow<R>, R);
+    load_rows<R, PAIR>(ms, row0, kk, row_bytes, BK, w, hs, KW, R);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_setprio(1);  // every row is requested: only decoding is left
