@@ -805,6 +805,106 @@ def trace_summary(trace_path, bench_json_path, command):
     log(f"summarized {len(rows)} dispatches of {csv_path} into profiles/kernel_trace.md and {TRACE_FILE}")
 
 
+def _read_counter_rows(path, counter):
+    """(dispatch order, kernel name, grid threads, workgroup, value) of every
+    dispatch in a rocprofv3 --pmc CSV for one counter."""
+    import csv
+    if os.path.isdir(path):
+        cands = [os.path.join(dp, f) for dp, _, fs in os.walk(path) for f in fs
+                 if f.endswith("counter_collection.csv")]
+        if len(cands) != 1:
+            raise SystemExit(f"expected one *counter_collection.csv under {path}, found {cands}")
+        path = cands[0]
+    out = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            grid = int(r.get("Grid_Size") or r.get("Grid_Size_X"))
+            wg = int(r.get("Workgroup_Size") or r.get("Workgroup_Size_X"))
+            prev = out.get(key)
+            val = float(r["Counter_Value"]) + (prev[4] if prev else 0.0)  # summed over dimensions
+            out[key] = (key, r["Kernel_Name"], grid, wg, val)
+    return [out[k] for k in sorted(out)], path
+
+
+def counter_summary(fetch_path, write_path, bench_json_path, commands):
+    """Calibrated HBM traffic of every timed section from two rocprofv3 --pmc
+    runs of bench.py --probes (FETCH_SIZE, then WRITE_SIZE), each scaled by
+    what the counter reads for the 1 GiB read-only grid-stride stream and the
+    256 MiB fill of the same run.  Writes profiles/TRAFFIC_FILE (the dominant
+    kernel) and profiles/hbm_traffic.md (every section)."""
+    with open(bench_json_path) as f:
+        line = next(ln for ln in f if ln.startswith("{"))
+    bench = json.loads(line)
+    markers = {int(k): v for k, v in bench["trace_markers"].items()}
+    per = {}
+    cal = {}
+    for counter, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
+        rows, _ = _read_counter_rows(path, counter)
+        current = None
+        for _, name, grid, wg, val in rows:
+            if "k_empty" in name and wg == 64 and (grid // 64) in markers:
+                current = markers[grid // 64]
+                continue
+            if "k_read_gridstride" in name or ("k_read(" in name and "blk" not in name):
+                cal.setdefault(counter + " read", []).append(val)
+            if "k_fill" in name:
+                cal.setdefault(counter + " fill", []).append(val)
+            if current is None:
+                continue
+            per.setdefault((current, name, grid), {}).setdefault(counter, []).append(val)
+    read_kib = max(cal["FETCH_SIZE read"])
+    fill_kib = max(cal["WRITE_SIZE fill"])
+    f_fetch = (1 << 30) / 1024 / read_kib
+    f_write = (1 << 28) / 1024 / fill_kib
+    sha = bench["provenance"]["kernel_source_sha"]
+    md = ["# HBM traffic per timed section of bench.py (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)", "",
+          "Commands (on the MI355X, from the repository root):", ""] + ["    " + c for c in commands] + [
+          "", f"Kernel source sha {sha}.  Calibration in the same runs: the 1 GiB read-only grid-stride stream "
+          f"reads {read_kib:.1f} KiB of FETCH_SIZE (factor {f_fetch:.5f}); the 256 MiB fill writes "
+          f"{fill_kib:.1f} KiB of WRITE_SIZE (factor {f_write:.5f}).  Per dispatch, averaged over the section's "
+          "dispatches of its most frequent kernel; algorithmic bytes as in the bench line (66/256 B per weight, "
+          "x read once, y written once).", "",
+          "| section | kernel | dispatches | FETCH KiB | WRITE KiB | calibrated bytes | algorithmic bytes | ratio |",
+          "|---|---|---|---|---|---|---|---|"]
+    algo = {"dominant kernel": algo_bytes(16384, 4096)}
+    for label, rec in (bench.get("configs") or {}).items():
+        algo[label] = rec["bytes_per_call"]
+    dominant = None
+    for (sec, name, grid), d in sorted(per.items(), key=lambda kv: -len(kv[1].get("FETCH_SIZE", []))):
+        if sec not in algo or "FETCH_SIZE" not in d or "WRITE_SIZE" not in d:
+            continue
+        fk = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"])
+        wk = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"])
+        b = fk * 1024 * f_fetch + wk * 1024 * f_write
+        md.append(f"| {sec} | `{name.split('(')[0]}` | {len(d['FETCH_SIZE'])} | {fk:.1f} | {wk:.1f} | {b:,.0f} | "
+                  f"{algo[sec]:,} | {b / algo[sec]:.3f} |")
+        algo.pop(sec)
+        if sec == "dominant kernel":
+            dominant = {"kernel": name, "kernel_source_sha": sha, "commands": commands,
+                        "fetch_size_kib_per_dispatch": round(fk, 1), "write_size_kib_per_dispatch": round(wk, 1),
+                        "dispatches_averaged": len(d["FETCH_SIZE"]),
+                        "calibration": {"read_probe": {"kernel": "k_read_gridstride (16-byte non-temporal stream)",
+                                                       "bytes": 1 << 30, "fetch_size_kib": round(read_kib, 1),
+                                                       "factor": round(f_fetch, 5)},
+                                        "fill_probe": {"kernel": "k_fill (16-byte stores)", "bytes": 1 << 28,
+                                                       "write_size_kib": round(fill_kib, 1),
+                                                       "factor": round(f_write, 5)}},
+                        "traffic_bytes_per_launch": int(round(b)),
+                        "algorithmic_bytes_per_launch": algo_bytes(16384, 4096),
+                        "traffic_over_algorithmic": round(b / algo_bytes(16384, 4096), 4)}
+    if dominant is None:
+        raise SystemExit("no counters for the dominant-kernel section")
+    with open(os.path.join(ROOT, "profiles", TRAFFIC_FILE), "w") as f:
+        json.dump(dominant, f, indent=1)
+        f.write("\n")
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    log(f"traffic of the dominant kernel: {dominant['traffic_over_algorithmic']} x algorithmic")
+
+
 def trace_kernel_us(trace, section):
     """Mean kernel duration (us) of the section's most frequent kernel."""
     if not trace or section not in trace["sections"] or not trace["sections"][section]:
@@ -834,10 +934,16 @@ def main():
     ap.add_argument("--trace-summary", help="(CPU) summarize a rocprofv3 kernel trace of this bench")
     ap.add_argument("--trace-json", help="the bench JSON line of the traced run (with --trace-summary)")
     ap.add_argument("--trace-command", default="", help="the traced command, recorded in the summary")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="(CPU) calibrated HBM traffic from two rocprofv3 --pmc runs of this bench with --probes")
+    ap.add_argument("--counter-commands", nargs="*", default=[], help="the two profiled commands")
     args = ap.parse_args()
 
     if args.trace_summary:
         trace_summary(args.trace_summary, args.trace_json, args.trace_command)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary[0], args.counter_summary[1], args.trace_json, args.counter_commands)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -935,6 +1041,7 @@ def main():
             for _ in range(3):
                 probes.fill(buf.data_ptr(), (1 << 30) // 4, 7)
                 probes.read(buf.data_ptr(), 1 << 30, ("gs", 2048))
+            torch.cuda.synchronize()
             torch.cuda.synchronize()
             del buf
         del step_graph, dom_graph

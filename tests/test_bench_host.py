@@ -100,3 +100,40 @@ def test_trace_summary_splits_sections_at_markers(tmp_path, monkeypatch):
     assert dom["dispatches"] == 2 and dom["mean_us"] == 5.5 and dom["grid_threads"] == 131072
     assert bench.trace_kernel_us(rec, bench.CONFIGS[4][0]) == (6.0, rows[6][0])
     assert bench.trace_kernel_us(rec, "decode step") == (None, None)
+
+
+def test_counter_summary_calibrates_and_attributes(tmp_path, monkeypatch):
+    """Synthetic rocprofv3 --pmc CSVs: the dominant kernel's FETCH/WRITE are
+    averaged over its section, scaled by the probes' factors (the 1 GiB read
+    reading half its bytes gives factor 2), and tied to the kernel source."""
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    hdr = "Dispatch_Id,Kernel_Name,Grid_Size,Workgroup_Size,Counter_Name,Counter_Value\n"
+
+    def csv(counter, rows):
+        d = tmp_path / counter
+        d.mkdir()
+        (d / "run_counter_collection.csv").write_text(
+            hdr + "".join(f"{i},\"{n}\",{g},{w},{counter},{v}\n" for i, (n, g, w, v) in enumerate(rows)))
+        return str(d)
+
+    dom = "tq2::k_gemv_f16<8, 1, 512, 0, true>(tq2::MatSet, long)"
+    common = [("k_empty()", 64 * bench.MARK_DOMINANT, 64, 0)]
+    fetch = csv("FETCH_SIZE", common + [(dom, 131072, 256, 8500.0), (dom, 131072, 256, 8520.0),
+                                        ("k_empty()", 64 * bench.MARK_END, 64, 0),
+                                        ("(anonymous namespace)::k_read_gridstride(x)", 524288, 256, 524288.0),
+                                        ("(anonymous namespace)::k_fill(x)", 524288, 256, 0.0)])
+    write = csv("WRITE_SIZE", common + [(dom, 131072, 256, 64.0), (dom, 131072, 256, 64.0),
+                                        ("k_empty()", 64 * bench.MARK_END, 64, 0),
+                                        ("(anonymous namespace)::k_read_gridstride(x)", 524288, 256, 0.0),
+                                        ("(anonymous namespace)::k_fill(x)", 524288, 256, 262144.0)])
+    js = tmp_path / "b.json"
+    js.write_text(json.dumps({"trace_markers": {str(bench.MARK_DOMINANT): "dominant kernel",
+                                                str(bench.MARK_END): None},
+                              "provenance": {"kernel_source_sha": "abc"}, "configs": {}}) + "\n")
+    bench.counter_summary(fetch, write, str(js), ["cmd1", "cmd2"])
+    rec = json.loads((tmp_path / "profiles" / bench.TRAFFIC_FILE).read_text())
+    assert rec["kernel_source_sha"] == "abc" and rec["dispatches_averaged"] == 2
+    assert rec["calibration"]["read_probe"]["factor"] == 2.0
+    assert rec["traffic_bytes_per_launch"] == round(8510.0 * 1024 * 2 + 64 * 1024)
+    assert bench.traffic_from_profiles("abc") == rec["traffic_bytes_per_launch"]
