@@ -38,8 +38,11 @@ Trace markers: before each timed section the bench launches an empty kernel
 whose workgroup count names the section (`trace_markers` in the JSON), so
 one rocprofv3 kernel trace of the bench splits into per-section kernel
 durations; `--trace-summary` (CPU only) turns such a trace into
-profiles/kernel_trace.md and profiles/kernel_trace.json, which later runs
-on the same kernel source read back as `us_per_launch_trace` / `trace_us`.
+profiles/matvec_bench_sections_kernel_trace.{md,json}, which later runs on
+the same kernel source read back as `us_per_launch_trace` / `trace_us`.
+`--counter-summary`, `--counter-table` and `--sweep-summary` (CPU only) write
+the calibrated HBM traffic, per-section counter tables and the read-probe
+sweep under profiles/ from rocprofv3 --pmc runs and a --probe-sweep line.
 """
 import argparse
 import ctypes
@@ -62,7 +65,7 @@ PROJ = [("q", 4096, 4096), ("k", 256, 4096), ("v", 256, 4096), ("o", 4096, 4096)
 DOMINANT = ("gate", "up")
 DOMINANT_KERNEL = "tq2::k_gemv_f16<8, 1, 512, 0, true> (gate and up, 16384x4096)"
 TRAFFIC_FILE = "gemv_f16_gate_up_16384x4096_traffic.json"
-TRACE_FILE = "kernel_trace.json"
+TRACE_FILE = "matvec_bench_sections_kernel_trace.json"
 METRIC = "tq2_gemv achieved HBM GB/s and % of MI355X peak; 224-linear decode steps/sec"
 STEP_SEEDS = {"weights": "10000 + 7*layer + proj", "x": "20000 + 7*layer + proj"}
 
@@ -759,7 +762,7 @@ def _read_trace_rows(path):
 
 def trace_summary(trace_path, bench_json_path, command):
     """Split a rocprofv3 kernel trace of bench.py at its marker kernels and
-    write profiles/kernel_trace.md and profiles/kernel_trace.json."""
+    write profiles/matvec_bench_sections_kernel_trace.{md,json}."""
     import numpy as np
     with open(bench_json_path) as f:
         line = next(ln for ln in f if ln.startswith("{"))
@@ -800,9 +803,9 @@ def trace_summary(trace_path, bench_json_path, command):
     with open(os.path.join(ROOT, "profiles", TRACE_FILE), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    with open(os.path.join(ROOT, "profiles", "kernel_trace.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", "matvec_bench_sections_kernel_trace.md"), "w") as f:
         f.write("\n".join(md) + "\n")
-    log(f"summarized {len(rows)} dispatches of {csv_path} into profiles/kernel_trace.md and {TRACE_FILE}")
+    log(f"summarized {len(rows)} dispatches of {csv_path} into profiles/{TRACE_FILE} and its .md")
 
 
 def _read_counter_rows(path, counter):
@@ -834,7 +837,7 @@ def counter_summary(fetch_path, write_path, bench_json_path, commands):
     runs of bench.py --probes (FETCH_SIZE, then WRITE_SIZE), each scaled by
     what the counter reads for the 1 GiB read-only grid-stride stream and the
     256 MiB fill of the same run.  Writes profiles/TRAFFIC_FILE (the dominant
-    kernel) and profiles/hbm_traffic.md (every section)."""
+    kernel) and profiles/matvec_bench_sections_hbm_traffic.md (every section)."""
     with open(bench_json_path) as f:
         line = next(ln for ln in f if ln.startswith("{"))
     bench = json.loads(line)
@@ -879,7 +882,7 @@ def counter_summary(fetch_path, write_path, bench_json_path, commands):
         fk = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"])
         wk = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"])
         b = fk * 1024 * f_fetch + wk * 1024 * f_write
-        md.append(f"| {sec} | `{name.split('(')[0]}` | {len(d['FETCH_SIZE'])} | {fk:.1f} | {wk:.1f} | {b:,.0f} | "
+        md.append(f"| {sec} | `{_kernel_short(name)}` | {len(d['FETCH_SIZE'])} | {fk:.1f} | {wk:.1f} | {b:,.0f} | "
                   f"{algo[sec]:,} | {b / algo[sec]:.3f} |")
         algo.pop(sec)
         if sec == "dominant kernel":
@@ -900,9 +903,101 @@ def counter_summary(fetch_path, write_path, bench_json_path, commands):
     with open(os.path.join(ROOT, "profiles", TRAFFIC_FILE), "w") as f:
         json.dump(dominant, f, indent=1)
         f.write("\n")
-    with open(os.path.join(ROOT, "profiles", "hbm_traffic.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", "matvec_bench_sections_hbm_traffic.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     log(f"traffic of the dominant kernel: {dominant['traffic_over_algorithmic']} x algorithmic")
+
+
+def _kernel_short(name):
+    """A kernel's name without its parameter list."""
+    if not name.endswith(")"):
+        return name
+    depth = 0
+    for i in range(len(name) - 1, -1, -1):
+        depth += {")": 1, "(": -1}.get(name[i], 0)
+        if depth == 0:
+            return name[:i]
+    return name
+
+
+def sweep_summary(bench_json_path, command):
+    """profiles/read_probe_sweep_17MB_35MB_1GiB.md from a bench run with --probe-sweep."""
+    with open(bench_json_path) as f:
+        line = next(ln for ln in f if ln.startswith("{"))
+    bench = json.loads(line)
+    rows = bench["read_probe_sweep"]
+    sizes = sorted({r["bytes"] for r in rows})
+    variants = []
+    for r in rows:
+        if r["variant"] not in variants:
+            variants.append(r["variant"])
+    by = {(r["variant"], r["bytes"]): r for r in rows}
+    md = ["# Read-only stream probes (achievable HBM read rate per dispatch)", "",
+          "Command (on the MI355X, from the repository root):", "", "    " + command, "",
+          f"{bench['provenance']['gpu']['name'] or 'MI355X'} {bench['provenance']['gpu']['arch']}; probe source in "
+          f"ternary_packed_weight_amd/csrc/tq2_probes.hip (source sha {bench['provenance']['source_sha']}).  Each "
+          "size is read from rotating copies totalling >= 1.1 GB (one graph touches every copy once), median of 5 "
+          "replays, us per dispatch with the dispatch included.  An empty kernel costs "
+          f"{bench['dispatch_floor_us']} us per graph node in the same run.", "",
+          "| variant | " + " | ".join(f"{b / 1e6:.1f} MB us | GB/s | % of 8 TB/s" for b in sizes) + " |",
+          "|---|" + "---|---|---|" * len(sizes)]
+    for v in variants:
+        cells = []
+        for b in sizes:
+            r = by.get((v, b))
+            cells += ([f"{r['us']}", f"{r['GB_s']}", f"{100 * r['GB_s'] / PEAK_HBM_GBS:.1f}"] if r else ["", "", ""])
+        md.append(f"| {v} | " + " | ".join(cells) + " |")
+    best = {b: min((r for r in rows if r["bytes"] == b), key=lambda r: r["us"]) for b in sizes}
+    md += ["", "Fastest per size: " + "; ".join(f"{b / 1e6:.1f} MB: {best[b]['variant']}, {best[b]['us']} us "
+                                                 f"({best[b]['GB_s']} GB/s)" for b in sizes) + "."]
+    with open(os.path.join(ROOT, "profiles", "read_probe_sweep_17MB_35MB_1GiB.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
+def counter_table(path, bench_json_path, command, out_name):
+    """Mean value of every counter of a rocprofv3 --pmc run of this bench,
+    per timed section and kernel (split at the trace markers), as
+    profiles/<out_name>."""
+    import csv
+    with open(bench_json_path) as f:
+        line = next(ln for ln in f if ln.startswith("{"))
+    bench = json.loads(line)
+    markers = {int(k): v for k, v in bench["trace_markers"].items()}
+    if os.path.isdir(path):
+        path = next(os.path.join(dp, f) for dp, _, fs in os.walk(path) for f in fs
+                    if f.endswith("counter_collection.csv"))
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            key = int(r["Dispatch_Id"])
+            e = rows.setdefault(key, {"name": r["Kernel_Name"], "grid": int(r.get("Grid_Size") or r.get("Grid_Size_X")),
+                                      "wg": int(r.get("Workgroup_Size") or r.get("Workgroup_Size_X")), "c": {}})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg, names, current = {}, [], None
+    for key in sorted(rows):
+        e = rows[key]
+        if "k_empty" in e["name"] and e["wg"] == 64 and (e["grid"] // 64) in markers:
+            current = markers[e["grid"] // 64]
+            continue
+        if current is None:
+            continue
+        a = agg.setdefault((current, _kernel_short(e["name"]), e["grid"]), {})
+        for c, v in e["c"].items():
+            a.setdefault(c, []).append(v)
+            if c not in names:
+                names.append(c)
+    md = [f"# rocprofv3 counters per timed section of bench.py ({', '.join(names)})", "",
+          "Command (on the MI355X, from the repository root):", "", "    " + command, "",
+          f"Kernel source sha {bench['provenance']['kernel_source_sha']}.  Mean per dispatch over the section's "
+          "dispatches, per kernel and grid.", "",
+          "| section | kernel | grid (threads) | dispatches | " + " | ".join(names) + " |",
+          "|---|---|---|---|" + "---|" * len(names)]
+    for (sec, name, grid), a in agg.items():
+        n = len(next(iter(a.values())))
+        md.append(f"| {sec} | `{name}` | {grid} | {n} | " +
+                  " | ".join(f"{sum(a[c]) / len(a[c]):.2f}" if c in a else "" for c in names) + " |")
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
+        f.write("\n".join(md) + "\n")
 
 
 def trace_kernel_us(trace, section):
@@ -937,6 +1032,9 @@ def main():
     ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="(CPU) calibrated HBM traffic from two rocprofv3 --pmc runs of this bench with --probes")
     ap.add_argument("--counter-commands", nargs="*", default=[], help="the two profiled commands")
+    ap.add_argument("--sweep-summary", help="(CPU) the read-probe sweep table under profiles/ from a --probe-sweep JSON line")
+    ap.add_argument("--counter-table", nargs=2, metavar=("PMC_DIR", "OUT_MD"),
+                    help="(CPU) per-section mean of every counter of one rocprofv3 --pmc run")
     args = ap.parse_args()
 
     if args.trace_summary:
@@ -944,6 +1042,12 @@ def main():
         return
     if args.counter_summary:
         counter_summary(args.counter_summary[0], args.counter_summary[1], args.trace_json, args.counter_commands)
+        return
+    if args.sweep_summary:
+        sweep_summary(args.sweep_summary, args.trace_command)
+        return
+    if args.counter_table:
+        counter_table(args.counter_table[0], args.trace_json, args.trace_command, args.counter_table[1])
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
