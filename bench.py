@@ -385,6 +385,7 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
     ("c3 down 4096x16384 int8 (fused quantize)", 4096, 16384, "i8", 1004),
     ("c3q down 4096x16384 int8, pre-quantized x_q (tq2_gemv_i8q)", 4096, 16384, "i8q", 1004),
     ("batched gate 16384x4096, 16 tokens per call (tq2_gemm)", 16384, 4096, "gemm16", 1005),
+    ("batched gate 16384x4096, 1 token per call (tq2_gemm)", 16384, 4096, "gemm1", 1005),
     # the adjacent entry points, each a single call on its own shape
     ("next: fused q/k/v 4096+256+256 x 4096 fp16 (tq2_gemv_fused)", 4096, 4096, "qkv", 1006),
     ("next: fused q/k/v 4096+256+256 x 4096 int8 (tq2_gemv_i8_fused)", 4096, 4096, "qkv_i8", 1006),
@@ -396,6 +397,7 @@ ROTATION_BYTES = 1.1e9  # > the 256 MB Infinity Cache: every timed call streams 
 WARM_REPLAYS = 10  # untimed graph replays before each configuration's timed ones (the first replays after setup run slower)
 REQUANT_S_OUT = 0.05
 CPU_TIMED_KINDS = ("f16", "f16_out", "gate_up", "i8", "i8q")
+GEMM_TOKENS = {"gemm16": 16, "gemm1": 1}
 
 
 def config_bytes(kind, N, K, rows):
@@ -404,8 +406,8 @@ def config_bytes(kind, N, K, rows):
         return 2 * N * K * 66 // 256 + 2 * K + 4 * N  # h = silu(gate) * up written once
     if kind == "requant":
         return N * K * 66 // 256 + 2 * K + N  # int8 output
-    if kind == "gemm16":
-        return N * K * 66 // 256 + 16 * (2 * K + 4 * N)  # weights once, 16 x and 16 y
+    if kind in GEMM_TOKENS:
+        return N * K * 66 // 256 + GEMM_TOKENS[kind] * (2 * K + 4 * N)  # weights once, M x and M y
     if kind == "i8q":
         return N * K * 66 // 256 + 4 * N + K  # x_q read once (1 byte per element)
     return sum(Ni * K * 66 // 256 + 4 * Ni for Ni in rows) + 2 * K  # x read once
@@ -440,15 +442,15 @@ class ConfigCase:
         # s = fp32(max|x|) / 100 in fp32 (IEEE division), as the workload states
         self.s = float(np.float32(np.abs(self.x_host.astype(np.float32)).max()) / np.float32(100))
         self.X16 = None
-        if kind == "gemm16":
-            self.X16 = torch.stack([synth.torch_activations(seed + 1 + m, K) for m in range(16)])
+        if kind in GEMM_TOKENS:
+            self.X16 = torch.stack([synth.torch_activations(seed + 1 + m, K) for m in range(GEMM_TOKENS[kind])])
         self.xq = tq2.tq2_quantize_i8(x, self.s) if kind == "i8q" else None
         self.nbytes = config_bytes(kind, N, K, self.rows)
         self.wbytes = sum(self.rows) * K * 66 // 256
 
     def out_buffer(self, torch):
-        if self.kind == "gemm16":
-            return torch.empty(16, self.N, dtype=torch.float32, device="cuda")
+        if self.kind in GEMM_TOKENS:
+            return torch.empty(GEMM_TOKENS[self.kind], self.N, dtype=torch.float32, device="cuda")
         if self.kind == "requant":
             return torch.empty(self.N, dtype=torch.int8, device="cuda")
         if self.kind == "silu":
@@ -461,7 +463,7 @@ class ConfigCase:
             return tq2.tq2_gemv(mats[0][0], mats[0][1], x, y=y)
         if k == "gate_up":
             return tq2.tq2_gemv_gate_up(mats[0][0], mats[0][1], mats[1][0], mats[1][1], x, y=y)
-        if k == "gemm16":
+        if k in GEMM_TOKENS:
             return tq2.tq2_gemm(mats[0][0], mats[0][1], x, y=y, ws=ws)
         if k == "qkv":
             return tq2.tq2_gemv_fused(mats, x, y=y)
@@ -478,7 +480,7 @@ class ConfigCase:
         return tq2.tq2_gemv_i8(mats[0][0], mats[0][1], x, self.s, y=y)
 
     def activation(self):
-        if self.kind == "gemm16":
+        if self.kind in GEMM_TOKENS:
             return self.X16
         if self.kind == "i8q":
             return self.xq
@@ -552,12 +554,12 @@ class ConfigCase:
             rec.update(rule="fp16 bounds of g and u propagated through silu(g)*u", max_err_over_bound=round(r, 6),
                        passed=r <= 1.0)
         else:
-            assert kind == "gemm16"
+            assert kind in GEMM_TOKENS
             ch, sh = packed[0]
             Xh = self.X16.cpu().numpy()
             ref = oracle.gemm(ch, sh, self.N, K, synth.bits(Xh))
             worst = 0.0
-            for m in range(16):
+            for m in range(GEMM_TOKENS[kind]):
                 tol = tol_f16(sh, Xh[m], self.N, K)
                 worst = max(worst, float((np.abs(yg[m].astype(np.float64) - ref[m]) / tol).max()))
             fns = []
@@ -613,8 +615,9 @@ def time_configs(torch, tq2, synth, probes, reps, max_calls, with_cpu):
         case = ConfigCase(torch, tq2, synth, label, N, K, kind, seed, want_host=with_cpu)
         rec = {"bytes_per_call": int(case.nbytes)}
         ws = None
-        if kind == "gemm16":
-            ws = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(N, K, 16)), dtype=torch.uint8, device="cuda")
+        if kind in GEMM_TOKENS:
+            ws = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(N, K, GEMM_TOKENS[kind])), dtype=torch.uint8,
+                             device="cuda")
         # parity and CPU timing on copy 0 (the originally packed buffers)
         if with_cpu:
             y0 = case.out_buffer(torch)
@@ -647,8 +650,8 @@ def time_configs(torch, tq2, synth, probes, reps, max_calls, with_cpu):
                     "pct_of_read_probe": round(100 * us_rd / us, 1),
                     "rotation_copies": ncopy, "calls_per_graph": ncall,
                     "bytes_rotated": int(ncall * case.nbytes), "trace_marker": MARK_CONFIG + ci})
-        if kind == "gemm16":
-            rec["tokens_per_s"] = round(16e6 / us, 1)
+        if kind in GEMM_TOKENS:
+            rec["tokens_per_s"] = round(GEMM_TOKENS[kind] * 1e6 / us, 1)
         if "cpu_oracle" in rec:
             rec["gpu_speedup_vs_cpu_nproc"] = round(rec["cpu_oracle"]["us_per_call_nproc"] / us, 1)
         out[label] = rec
@@ -1165,8 +1168,9 @@ def main():
             rec["trace_us"] = t_us
             rec["trace_pct_of_peak_hbm"] = None if t_us is None else round(
                 100 * rec["bytes_per_call"] / t_us / 1e3 / PEAK_HBM_GBS, 2)
-            if CONFIGS[ci][3] == "gemm16" and stack is not None:
-                rec["speedup_vs_16_gemv"] = round(16 * out["roofline"]["us_per_launch"] / rec["us_per_call"], 2)
+            if CONFIGS[ci][3] in GEMM_TOKENS and stack is not None:
+                m = GEMM_TOKENS[CONFIGS[ci][3]]
+                rec[f"speedup_vs_{m}_gemv"] = round(m * out["roofline"]["us_per_launch"] / rec["us_per_call"], 2)
         c0, c1 = (out["configs"][CONFIGS[i][0]]["us_per_call"] for i in (0, 1))
         qkv = next(out["configs"][c[0]] for c in CONFIGS if c[3] == "qkv")
         qkv["three_single_calls_us"] = round(c1 + 2 * c0, 3)

@@ -224,7 +224,9 @@ size_t tq2_gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);
  * not overlapping X or Y (TQ2_ERR_WORKSPACE otherwise); its contents on
  * entry do not matter and are overwritten.  Otherwise ws may be NULL.  One
  * kernel on `stream` (two when K is split); deterministic (chunk and split
- * sums are added in a fixed order). */
+ * sums are added in a fixed order).  M = 1 runs tq2_gemv's kernel (no
+ * workspace; the output equals tq2_gemv's bit for bit); for M >= 2 a token's
+ * output does not depend on the other tokens of the call. */
 #define TQ2_MAX_TOKENS 65536
 int32_t tq2_gemm(const uint8_t *codes, const uint16_t *scales, int64_t N,
                  int64_t K, const uint16_t *x, int64_t M, float *y, void *ws,

@@ -1131,12 +1131,25 @@ GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
 }
 
 size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+  if (M == 1) return 0;  // the one-token matvec (see launch_gemm)
   const GemmPlan p = plan_gemm(N, K, M);
   return (size_t)p.part_bytes;
 }
 
 hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                        const uint16_t* x, int64_t M, float* y, void* ws, hipStream_t st) {
+  if (M == 1) {
+    // one token: the VALU matvec, which streams the weights without the
+    // matrix-core tile's per-step x staging (measured on MI355X: 16384x4096
+    // one token 9.4-9.6 us through k_gemm_mfma, 5.2-5.3 us through
+    // k_gemv_f16)
+    MatSet m{};
+    m.codes[0] = codes;
+    m.scales[0] = scales;
+    m.nmat = 1;
+    m.rows = (int32_t)N;
+    return launch_gemv_f16(m, K, x, y, st);
+  }
   const GemmPlan p = plan_gemm(N, K, M);
   float* part = static_cast<float*>(ws);
   GemmArgs a;

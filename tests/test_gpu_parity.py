@@ -576,8 +576,9 @@ def test_gemm_parity(tq2, N, K, M):
 def test_gemm_token_independence_and_determinism(tq2):
     """A token's output does not depend on the other tokens of the call, and
     repeated calls are bitwise identical (split partials added in order).
-    16 tokens stage x through LDS, 1 token loads it per lane: the two ways
-    must give the same bits."""
+    16 tokens stage x through LDS, 2 tokens load it per lane: the two ways
+    must give the same bits.  One token runs the matvec kernel: bit-equal to
+    tq2_gemv."""
     N, K = 4096, 16384
     _, c, s, _ = _packed(1950, N, K)
     g = synth.rng(1951)
@@ -586,11 +587,14 @@ def test_gemm_token_independence_and_determinism(tq2):
     Xd = torch.from_numpy(np.ascontiguousarray(X, np.float16)).to(DEV)
     Y1 = tq2.tq2_gemm(dc, ds, Xd)
     Y2 = tq2.tq2_gemm(dc, ds, Xd)
-    Y3 = tq2.tq2_gemm(dc, ds, Xd[5:6].contiguous())
+    Y3 = tq2.tq2_gemm(dc, ds, Xd[4:6].contiguous())
+    Y4 = tq2.tq2_gemm(dc, ds, Xd[5:6].contiguous())
     Yv = tq2.tq2_gemv(dc, ds, Xd[5].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
-    assert torch.equal(Y1[5], Y3[0])
+    assert torch.equal(Y1[5], Y3[1])
+    assert torch.equal(Y4[0], Yv)
+    assert tq2.tq2_gemm_workspace_bytes(N, K, 1) == 0
     _check_f16(Y1[5].cpu().numpy(), Yv.cpu().numpy().astype(np.float64), 2 * _tol(s, X[5], N, K))
 
 
