@@ -744,14 +744,26 @@ def fused_step(torch, tq2, stack, steps, probes):
 
 # ----------------------------------------------------- trace summary (CPU)
 
+def _find_csv(path, suffix):
+    """The one <...>suffix (or suffix.gz) file under a directory, or path."""
+    if not os.path.isdir(path):
+        return path
+    cands = [os.path.join(dp, f) for dp, _, fs in os.walk(path) for f in fs
+             if f.endswith(suffix) or f.endswith(suffix + ".gz")]
+    if len(cands) != 1:
+        raise SystemExit(f"expected one *{suffix} under {path}, found {cands}")
+    return cands[0]
+
+
+def _open_csv(path):
+    import gzip
+    return gzip.open(path, "rt", newline="") if path.endswith(".gz") else open(path, newline="")
+
+
 def _read_trace_rows(path):
     import csv
-    if os.path.isdir(path):
-        cands = [os.path.join(dp, f) for dp, _, fs in os.walk(path) for f in fs if f.endswith("kernel_trace.csv")]
-        if len(cands) != 1:
-            raise SystemExit(f"expected one *kernel_trace.csv under {path}, found {cands}")
-        path = cands[0]
-    with open(path, newline="") as f:
+    path = _find_csv(path, "kernel_trace.csv")
+    with _open_csv(path) as f:
         rows = list(csv.DictReader(f))
     grid_key = next(k for k in ("Grid_Size_X", "Grid_Size", "Grid_Sizes_X") if k in rows[0])
     wg_key = next(k for k in ("Workgroup_Size_X", "Workgroup_Size", "Workgroup_Sizes_X") if k in rows[0])
@@ -815,14 +827,9 @@ def _read_counter_rows(path, counter):
     """(dispatch order, kernel name, grid threads, workgroup, value) of every
     dispatch in a rocprofv3 --pmc CSV for one counter."""
     import csv
-    if os.path.isdir(path):
-        cands = [os.path.join(dp, f) for dp, _, fs in os.walk(path) for f in fs
-                 if f.endswith("counter_collection.csv")]
-        if len(cands) != 1:
-            raise SystemExit(f"expected one *counter_collection.csv under {path}, found {cands}")
-        path = cands[0]
+    path = _find_csv(path, "counter_collection.csv")
     out = {}
-    with open(path, newline="") as f:
+    with _open_csv(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
@@ -966,11 +973,9 @@ def counter_table(path, bench_json_path, command, out_name):
         line = next(ln for ln in f if ln.startswith("{"))
     bench = json.loads(line)
     markers = {int(k): v for k, v in bench["trace_markers"].items()}
-    if os.path.isdir(path):
-        path = next(os.path.join(dp, f) for dp, _, fs in os.walk(path) for f in fs
-                    if f.endswith("counter_collection.csv"))
+    path = _find_csv(path, "counter_collection.csv")
     rows = {}
-    with open(path, newline="") as f:
+    with _open_csv(path) as f:
         for r in csv.DictReader(f):
             key = int(r["Dispatch_Id"])
             e = rows.setdefault(key, {"name": r["Kernel_Name"], "grid": int(r.get("Grid_Size") or r.get("Grid_Size_X")),
