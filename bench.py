@@ -394,7 +394,15 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
 ]
 QKV_ROWS = (4096, 256, 256)
 ROTATION_BYTES = 1.1e9  # > the 256 MB Infinity Cache: every timed call streams from HBM
-WARM_REPLAYS = 10  # untimed graph replays before each configuration's timed ones (the first replays after setup run slower)
+# Untimed replays before each configuration's timed ones: at least
+# WARM_REPLAYS and at least WARM_SECONDS of them.  Each configuration is
+# timed right after its CPU parity check and CPU timing, seconds in which the
+# GPU idles; its clocks then take longer than a few milliseconds of work to
+# come back (measured on MI355X: the fused gate+up timed 9.1-9.3 us in the
+# first round after such a pause and 8.3-8.4 us in the rounds after it, with
+# 10 warm replays, ~3 ms, before each).
+WARM_REPLAYS = 10
+WARM_SECONDS = 0.25
 REQUANT_S_OUT = 0.05
 CPU_TIMED_KINDS = ("f16", "f16_out", "gate_up", "i8", "i8q")
 GEMM_TOKENS = {"gemm16": 16, "gemm1": 1}
@@ -577,12 +585,27 @@ def rotation(nbytes, max_calls):
     return ncopy, (ncopy if max_calls is None else min(ncopy, max_calls))
 
 
+def warm(torch, g):
+    """Untimed replays of g: at least WARM_REPLAYS, and until at least
+    WARM_SECONDS have passed (synchronizing every few replays, so that the
+    host clock follows the GPU)."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < WARM_REPLAYS or time.perf_counter() - t0 < WARM_SECONDS:
+        g.replay()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def time_rotating(torch, probes, calls, reps, mark):
     """Median and 95th percentile (us per call) over `reps` replays of one
-    graph holding every call once, after WARM_REPLAYS untimed replays."""
+    graph holding every call once, after the untimed replays of warm()."""
     import numpy as np
     g = capture(torch, calls)
-    time_graph(torch, g, WARM_REPLAYS)
+    warm(torch, g)
     if probes is not None:
         probes.marker(mark)
     ts = [time_graph(torch, g, 1) / len(calls) for _ in range(reps)]
@@ -1166,6 +1189,10 @@ def main():
     if not args.no_configs:
         with_cpu = not args.no_cpu
         out["configs"] = time_configs(torch, tq2, synth, probes, args.config_reps, args.config_calls, with_cpu)
+        out["configs_timing"] = (f"per configuration: one graph calling every rotating copy once; untimed replays "
+                                 f"(at least {WARM_REPLAYS}, and at least {WARM_SECONDS} s), then the median and "
+                                 f"95th percentile of {args.config_reps} timed replays (HIP events); the read probe "
+                                 f"beside it the same way")
         for label, rec in out["configs"].items():
             ci = next(i for i, c in enumerate(CONFIGS) if c[0] == label)
             t_us, kname = trace_kernel_us(trace, label)
