@@ -208,9 +208,10 @@ int32_t tq2_gemv_i8_requant(const uint8_t *codes, const uint16_t *scales,
 
 /* tq2_gemm_workspace_bytes -- device workspace that tq2_gemm needs for this
  * shape and token count: the split partials (4*M*N bytes per split) when the
- * plan splits K across workgroups, which it does only when N gives too few
- * row groups to fill the GPU; 0 otherwise.  (size_t)-1 for an invalid
- * shape or token count. */
+ * matrix-core plan splits K across workgroups, which it does only when N
+ * gives too few row groups to fill the GPU; 0 otherwise, and 0 whenever
+ * the call runs a matvec kernel (M = 1, and the few-token calls described
+ * at tq2_gemm).  (size_t)-1 for an invalid shape or token count. */
 size_t tq2_gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);
 
 /* tq2_gemm -- the matvec of page "BitCPM ternary (1.58-bit)" (kernel
@@ -225,8 +226,13 @@ size_t tq2_gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);
  * entry do not matter and are overwritten.  Otherwise ws may be NULL.  One
  * kernel on `stream` (two when K is split); deterministic (chunk and split
  * sums are added in a fixed order).  M = 1 runs tq2_gemv's kernel (no
- * workspace; the output equals tq2_gemv's bit for bit); for M >= 2 a token's
- * output does not depend on the other tokens of the call. */
+ * workspace; the output equals tq2_gemv's bit for bit).  M = 2 to 4 with K
+ * of 1, 2 or 4 chunks of 4096 runs a one-pass matvec that decodes every
+ * code word once for all M tokens, while the activations it stages over all
+ * its workgroups (workgroups x M x 2K bytes) stay within 32 MiB, which
+ * holds for small and medium N: no workspace, and every token's output
+ * equals tq2_gemv's bit for bit.  Other calls run on the matrix cores.  For M >= 2 a token's output does not depend on the other
+ * tokens of the call. */
 #define TQ2_MAX_TOKENS 65536
 int32_t tq2_gemm(const uint8_t *codes, const uint16_t *scales, int64_t N,
                  int64_t K, const uint16_t *x, int64_t M, float *y, void *ws,

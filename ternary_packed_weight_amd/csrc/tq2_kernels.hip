@@ -215,6 +215,50 @@ __device__ __forceinline__ float lane_dot_f16(const uint4 w, const uint32_t (&xp
   return __builtin_fmaf(a, 16.0f, b);
 }
 
+// lane_dot_f16 for M tokens at once: the masked code words are formed once
+// and each token runs lane_dot_f16's two chains on them, in the same order,
+// so every token's value is bit-equal to lane_dot_f16 on that token's x.
+template <int M>
+__device__ __forceinline__ void lane_dot_f16_m(const uint4 w, const uint32_t (&xp)[M][32],
+                                               const float (&seed)[M], float (&out)[M]) {
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+  uint32_t v8[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) v8[g] = v[g] >> 8;
+  uint32_t ma[2][4][2], mb[2][4][2];  // [jj][g][v or v8]
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const uint32_t ka = 0x00030003u << (2 * jj), kb = 0x00030003u << (2 * (jj + 2));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      ma[jj][g][0] = v[g] & ka;
+      ma[jj][g][1] = v8[g] & ka;
+      mb[jj][g][0] = v[g] & kb;
+      mb[jj][g][1] = v8[g] & kb;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < M; ++t) {
+    float a = dot2(xp[t][0], ma[0][0][0], seed[t]);
+    float b = dot2(xp[t][4], mb[0][0][0], 0.0f);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      if (jj) {
+        a *= 4.0f;
+        b *= 4.0f;
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (jj || g) a = dot2(xp[t][8 * g + 2 * jj + 0], ma[jj][g][0], a);
+        if (jj || g) b = dot2(xp[t][8 * g + 2 * (jj + 2) + 0], mb[jj][g][0], b);
+        a = dot2(xp[t][8 * g + 2 * jj + 1], ma[jj][g][1], a);
+        b = dot2(xp[t][8 * g + 2 * (jj + 2) + 1], mb[jj][g][1], b);
+      }
+    }
+    out[t] = __builtin_fmaf(a, 16.0f, b);
+  }
+}
+
 // ---- wave64 reduction of R per-lane values (one per row) ----
 // Transposed butterfly: v_permlane32_swap folds lanes 32..63 onto 0..31 for
 // two rows at once, v_permlane16_swap folds 16-lane rows likewise, and four
@@ -639,6 +683,174 @@ __global__ __launch_bounds__(MAXT) void k_gemv_f16(MatSet ms, int64_t K,
   }
 }
 
+// The matvec for M = 2..4 tokens (the small-M batched matvec): k_gemv_f16's
+// waves, rows, loads and order, with the M tokens' activations staged side
+// by side in LDS.  Each code word is masked once and then dotted with every
+// token's operand pairs (lane_dot_f16_m), so the weights are streamed and
+// decoded once for all M tokens.  Every token's arithmetic is k_gemv_f16's
+// on that token: its output equals tq2_gemv's bit for bit.  Output y[M][N].
+// staging passes of k_gemv_f16m: every group of 16 activations of the C
+// chunks gets a thread (MAXT is the block size the launcher uses)
+__host__ __device__ constexpr int f16m_stage_passes(int CT, int MAXT) {
+  return CT ? (CT * 256 + MAXT - 1) / MAXT : 4;
+}
+
+template <int M>
+__host__ __device__ inline size_t f16m_lds_bytes(int C, int S, int R) {
+  return (size_t)M * ((size_t)C * 8 * 64 * 16 + (size_t)C * 64 * 16) + 3 * 16 + (size_t)M * C * S * R * 4;
+}
+
+template <int R, int M, int CT, int MAXT, bool EAGER>
+__global__ __launch_bounds__(MAXT) void k_gemv_f16m(MatSet ms, int64_t K, const uint16_t* __restrict__ x,
+                                                    float* __restrict__ y, Split sp) {
+  extern __shared__ uint4 lds[];
+  constexpr int KW = (EAGER || R < 8) ? kRowWindow<R> : 1;
+  const int C = CT ? CT : sp.C, S = sp.S;
+  uint4* xpairs = lds;                                            // [M][C][8][64]
+  float4* gsum = reinterpret_cast<float4*>(lds + M * C * 8 * 64);  // [M][C][64]
+  uint4* sink = reinterpret_cast<uint4*>(gsum + M * C * 64);       // [3]
+  float* red = reinterpret_cast<float*>(sink + 3);                 // [M][C*S][R]
+  if constexpr (EAGER) __builtin_amdgcn_s_setprio(2);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = __builtin_amdgcn_readfirstlane(wave / C);
+  const int c = wave - slot * C;
+  const int row0 = ((int)blockIdx.x * S + slot) * R;
+  const int64_t k0 = (int64_t)c * kChunk + (int64_t)lane * kLaneK;
+  const bool active = k0 < K;
+  const int64_t kk = active ? k0 : 0;
+  const int64_t row_bytes = K / 4;
+  const int64_t BK = K / kBlock;
+  const int64_t N = ms.rows;
+
+  // (1) loads: every token's activations (as k_gemv_f16, per token), the
+  //     workgroup barrier, then the first KW rows
+  constexpr int XP = f16m_stage_passes(CT, MAXT);
+  uint4 xa[M][XP], xb[M][XP];
+#pragma unroll
+  for (int t = 0; t < M; ++t) {
+    const __amdgpu_buffer_rsrc_t xr = rsrc(x + t * K, (uint32_t)(K * 2));
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+      const int m = tid + p * (int)blockDim.x;
+      xa[t][p] = load_b128(xr, 32 * m);
+      xb[t][p] = load_b128(xr, 32 * m + 16);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();  // x of every wave ahead of any weight request (see k_gemv_f16)
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 w[R];
+  uint16_t hs[R];
+  load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs, 0, KW);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (EAGER) __builtin_amdgcn_s_setprio(0);
+
+  // (2) stage every token as k_gemv_f16 stages its one
+#pragma unroll
+  for (int t = 0; t < M; ++t) {
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+      const int m = tid + p * (int)blockDim.x;
+      const bool staged = m < C * 256;
+      const uint4 a4 = xa[t][p], b4 = xb[t][p];
+      const uint32_t xw[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+      uint32_t pr[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = xw[j >> 1], b = xw[4 + (j >> 1)];
+        const uint32_t cc = xw[2 + (j >> 1)], d = xw[6 + (j >> 1)];
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        pr[2 * j + 0] = __builtin_amdgcn_perm(b, a, sel);
+        pr[2 * j + 1] = __builtin_amdgcn_perm(d, cc, sel);
+      }
+      float s0 = dot2(xw[0], kOnesF16x2, 0.0f), s1 = dot2(xw[1], kOnesF16x2, 0.0f);
+      s0 = dot2(xw[2], kOnesF16x2, s0); s1 = dot2(xw[3], kOnesF16x2, s1);
+      s0 = dot2(xw[4], kOnesF16x2, s0); s1 = dot2(xw[5], kOnesF16x2, s1);
+      s0 = dot2(xw[6], kOnesF16x2, s0); s1 = dot2(xw[7], kOnesF16x2, s1);
+      const int ch = m >> 8, ln = (m >> 2) & 63, gg = m & 3;
+      uint4* d0 = staged ? xpairs + ((t * C + ch) * 8 + 2 * gg) * 64 + ln : sink;
+      uint4* d1 = staged ? xpairs + ((t * C + ch) * 8 + 2 * gg + 1) * 64 + ln : sink + 1;
+      float* d2 = staged ? reinterpret_cast<float*>(gsum) + ((t * C + ch) * 64 + ln) * 4 + gg
+                         : reinterpret_cast<float*>(sink + 2);
+      *d0 = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+      *d1 = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+      *d2 = s0 + s1;
+    }
+  }
+  __syncthreads();
+
+  // (3) this lane's operand pairs and seed per token, then the rest of the rows
+  uint32_t xp[M][32];
+  float seed[M];
+#pragma unroll
+  for (int t = 0; t < M; ++t) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 tt = xpairs[((t * C + c) * 8 + i) * 64 + lane];
+      xp[t][4 * i + 0] = tt.x; xp[t][4 * i + 1] = tt.y; xp[t][4 * i + 2] = tt.z; xp[t][4 * i + 3] = tt.w;
+    }
+    const float4 gs = gsum[(t * C + c) * 64 + lane];
+    seed[t] = -ldexpf((gs.x + gs.y) + (gs.z + gs.w), -24);
+  }
+  if constexpr (KW < R) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs, KW, R);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(1);
+
+  float acc[M][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t keep = row_valid<R, false>(ms, row0, r) ? 0xFFFFu : 0u;
+    const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hs[r] & keep));
+    // the row's code words pass through an empty asm here, so that its masked
+    // words are formed here and not hoisted ahead for all rows at once
+    uint4 wr = w[r];
+    asm volatile("" : "+v"(wr.x), "+v"(wr.y), "+v"(wr.z), "+v"(wr.w));
+    float dt[M];
+    lane_dot_f16_m<M>(wr, xp, seed, dt);
+#pragma unroll
+    for (int t = 0; t < M; ++t) acc[t][r] = __builtin_fmaf((float)d, dt[t], 0.0f);  // v_fma_mix
+    // one row's masked words live at a time (M tokens' operands take
+    // 32 M registers already)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int rho = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < M; ++t) {
+    float out[kOut<R>];
+    reduce_rows_f32<R>(acc[t], out);
+    if (C == 1) {
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < kOut<R>; ++i) {
+          const int rr = reduced_row<R>(i, rho);
+          if (rr >= 0 && row0 + rr < ms.rows) y[t * N + row0 + rr] = ldexpf(out[i], 18);
+        }
+      }
+    } else if ((lane & 15) == 0) {
+#pragma unroll
+      for (int i = 0; i < kOut<R>; ++i) {
+        const int rr = reduced_row<R>(i, rho);
+        if (rr >= 0) red[(t * C * S + wave) * R + rr] = out[i];
+      }
+    }
+  }
+  if (C == 1) return;
+  __syncthreads();
+  if (c == 0 && lane < R) {
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+      float tsum = red[(t * C * S + wave) * R + lane];
+      for (int cc = 1; cc < C; ++cc) tsum += red[(t * C * S + wave + cc) * R + lane];
+      if (row0 + lane < ms.rows) y[t * N + row0 + lane] = ldexpf(tsum, 18);
+    }
+  }
+}
+
 static int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -727,6 +939,74 @@ hipError_t launch_gemv_f16(const MatSet& m, int64_t K, const uint16_t* x, float*
     case 4: return run_gemv_f16<4, kStoreF32>(m, K, x, y, s);
     default: return run_gemv_f16<2, kStoreF32>(m, K, x, y, s);
   }
+}
+
+// The matvec for M = 2..4 tokens: k_gemv_f16m with fewer rows per wave
+// than tq2_gemv (4 for two tokens, 2 for three or four; M tokens' operands
+// take 32 M registers) and, for K = 16384, 8-wave workgroups, so that every
+// wave stays within 256 registers without spilling.  The results do not
+// depend on either choice: a row's 64 lane partials are added in the same
+// order for every rows-per-wave (lanes l and l+32, then l and l+16, then the
+// 16-lane rotations), and chunk sums in chunk order, so every token's output
+// still equals tq2_gemv's.  For K of 1, 2 or 4 chunks (the caller checks).
+template <int R, int M>
+static hipError_t run_gemv_f16m(const MatSet& m, int64_t K, const uint16_t* x, float* y, hipStream_t s) {
+  Split sp = pick_split(K, true);
+  if (sp.C != 1 && sp.C != 2 && sp.C != 4) return hipErrorInvalidConfiguration;
+  if (sp.C == 4) sp.S = 2;  // 512 threads: 256 registers per wave
+  const int64_t groups = (m.rows + R - 1) / R;
+  const int64_t nwg = (groups + sp.S - 1) / sp.S;
+  const bool eager = nwg <= 2LL * device_cus();
+  const dim3 grid((unsigned)nwg);
+  const size_t lds = f16m_lds_bytes<M>(sp.C, sp.S, R);
+  const dim3 block(64 * sp.C * sp.S);
+  // every instantiation below has MAXT = 512 and the block is exactly 512
+  // threads for C = 2 and 4, 256 for C = 1 (256 groups)
+  if ((int64_t)f16m_stage_passes(sp.C, 512) * block.x < (int64_t)sp.C * 256 || block.x > 512 ||
+      lds > 160 * 1024)
+    return hipErrorInvalidConfiguration;
+  auto go = [&](auto kfn) -> hipError_t {
+    if (lds > 64 * 1024) {
+      const hipError_t e = set_lds_cap(reinterpret_cast<const void*>(kfn));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kfn, grid, block, lds, s, m, K, x, y, sp);
+    return hipGetLastError();
+  };
+  if (eager) {
+    if (sp.C == 1) return go(k_gemv_f16m<R, M, 1, 512, true>);
+    if (sp.C == 2) return go(k_gemv_f16m<R, M, 2, 512, true>);
+    return go(k_gemv_f16m<R, M, 4, 512, true>);
+  }
+  if (sp.C == 1) return go(k_gemv_f16m<R, M, 1, 512, false>);
+  if (sp.C == 2) return go(k_gemv_f16m<R, M, 2, 512, false>);
+  return go(k_gemv_f16m<R, M, 4, 512, false>);
+}
+
+// rows per wave of k_gemv_f16m for M tokens (see run_gemv_f16m)
+static int f16m_rows_per_wave(int64_t rows, int64_t K, int64_t M) {
+  return pick_rows_per_wave(rows, (int)chunks_of(K), f16_waves_per_cu(K), M == 2 ? 4 : 2);
+}
+
+// Activation bytes k_gemv_f16m stages over all its workgroups (each stages
+// every token's whole x).  Measured on MI355X against the matrix-core path:
+// the one-pass kernel wins while this stays at or below 32 MiB (4096x4096
+// at 4 tokens 5.2 against 7.5 us, 16384x4096 at 2 tokens 8.1 against 9.1,
+// 4096x16384 at 2 tokens 9.9 against 11.7) and loses above (16384x4096 at
+// 3 and 4 tokens, 48 and 64 MiB: 11.8 and 14.0 against 9.3 us; 4096x16384
+// at 4 tokens, 128 MiB: 23.5 against 11.9).
+static int64_t f16m_staging_bytes(int64_t rows, int64_t K, int64_t M) {
+  const int R = f16m_rows_per_wave(rows, K, M);
+  Split sp = pick_split(K, true);
+  if (sp.C == 4) sp.S = 2;
+  const int64_t nwg = ((rows + R - 1) / R + sp.S - 1) / sp.S;
+  return nwg * M * K * 2;
+}
+
+template <int M>
+static hipError_t launch_gemv_f16m(const MatSet& m, int64_t K, const uint16_t* x, float* y, hipStream_t s) {
+  if (f16m_rows_per_wave(m.rows, K, M) == 4 && M == 2) return run_gemv_f16m<4, M>(m, K, x, y, s);
+  return run_gemv_f16m<2, M>(m, K, x, y, s);
 }
 
 hipError_t launch_gemv_silu_mul(const MatSet& m, int64_t K, const uint16_t* x, float* h,
@@ -1130,8 +1410,21 @@ GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
   return p;
 }
 
+// 2 to 4 tokens with K of 1, 2 or 4 chunks take the one-pass VALU matvec
+// (k_gemv_f16m) while its activation staging stays within 32 MiB: the
+// weights are then decoded once for the few tokens, where the matrix-core
+// tile computes 16 tokens whatever M is (9.1-9.7 us at 16384x4096 for 2 to
+// 16 tokens).
+constexpr int64_t kValuTokens = 4;
+constexpr int64_t kValuStagingBytes = (int64_t)32 << 20;
+static bool gemm_on_valu(int64_t N, int64_t K, int64_t M) {
+  const int64_t c = chunks_of(K);
+  return M >= 2 && M <= kValuTokens && (c == 1 || c == 2 || c == 4) &&
+         f16m_staging_bytes(N, K, M) <= kValuStagingBytes;
+}
+
 size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M) {
-  if (M == 1) return 0;  // the one-token matvec (see launch_gemm)
+  if (M == 1 || gemm_on_valu(N, K, M)) return 0;  // the matvec kernels (see launch_gemm)
   const GemmPlan p = plan_gemm(N, K, M);
   return (size_t)p.part_bytes;
 }
@@ -1149,6 +1442,16 @@ hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, 
     m.nmat = 1;
     m.rows = (int32_t)N;
     return launch_gemv_f16(m, K, x, y, st);
+  }
+  if (gemm_on_valu(N, K, M)) {
+    MatSet m{};
+    m.codes[0] = codes;
+    m.scales[0] = scales;
+    m.nmat = 1;
+    m.rows = (int32_t)N;
+    if (M == 2) return launch_gemv_f16m<2>(m, K, x, y, st);
+    if (M == 3) return launch_gemv_f16m<3>(m, K, x, y, st);
+    return launch_gemv_f16m<4>(m, K, x, y, st);
   }
   const GemmPlan p = plan_gemm(N, K, M);
   float* part = static_cast<float*>(ws);

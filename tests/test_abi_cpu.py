@@ -194,6 +194,18 @@ def test_gemm_workspace_only_for_split_k(tq2):
 
 
 @no_gpu
+def test_gemm_few_tokens_need_no_workspace(tq2):
+    """2 to 4 tokens with K of 1, 2 or 4 chunks of 4096 run the VALU matvec
+    (no workspace); other K, and more tokens, take the matrix-core plan."""
+    ws = tq2.lib().tq2_gemm_workspace_bytes
+    for K in (256, 4096, 4352, 8192, 16384):
+        for M in (2, 3, 4):
+            assert ws(256, K, M) == 0, (K, M)
+    assert ws(256, 4096, 5) > 0        # five tokens: matrix cores, K split for 256 rows
+    assert ws(256, 12288, 2) > 0       # three chunks: matrix cores
+
+
+@no_gpu
 def test_gemm_split_rule(tq2):
     """K is split only while the workgroups still fit one per CU (256 CUs):
     the workspace is splits x M x N fp32 partials, or 0 without a split."""

@@ -576,9 +576,10 @@ def test_gemm_parity(tq2, N, K, M):
 def test_gemm_token_independence_and_determinism(tq2):
     """A token's output does not depend on the other tokens of the call, and
     repeated calls are bitwise identical (split partials added in order).
-    16 tokens stage x through LDS, 2 tokens load it per lane: the two ways
-    must give the same bits.  One token runs the matvec kernel: bit-equal to
-    tq2_gemv."""
+    16 tokens (matrix cores) and 5 tokens (matrix cores, x loaded per lane)
+    give the same bits for a token; 1 and 2 tokens run the VALU matvec
+    kernels, bit-equal to tq2_gemv, and within the fp16 tolerance of the
+    matrix-core result."""
     N, K = 4096, 16384
     _, c, s, _ = _packed(1950, N, K)
     g = synth.rng(1951)
@@ -587,15 +588,54 @@ def test_gemm_token_independence_and_determinism(tq2):
     Xd = torch.from_numpy(np.ascontiguousarray(X, np.float16)).to(DEV)
     Y1 = tq2.tq2_gemm(dc, ds, Xd)
     Y2 = tq2.tq2_gemm(dc, ds, Xd)
+    Y5 = tq2.tq2_gemm(dc, ds, Xd[1:6].contiguous())
     Y3 = tq2.tq2_gemm(dc, ds, Xd[4:6].contiguous())
     Y4 = tq2.tq2_gemm(dc, ds, Xd[5:6].contiguous())
     Yv = tq2.tq2_gemv(dc, ds, Xd[5].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
-    assert torch.equal(Y1[5], Y3[1])
+    assert torch.equal(Y1[5], Y5[4])
+    assert torch.equal(Y3[1], Yv)
     assert torch.equal(Y4[0], Yv)
     assert tq2.tq2_gemm_workspace_bytes(N, K, 1) == 0
+    assert tq2.tq2_gemm_workspace_bytes(N, K, 2) == 0
     _check_f16(Y1[5].cpu().numpy(), Yv.cpu().numpy().astype(np.float64), 2 * _tol(s, X[5], N, K))
+
+
+# (N, K, M, one-pass VALU route): 2 to 4 tokens take it for K of 1, 2 or 4
+# chunks while all workgroups together stage at most 32 MiB of activations;
+# the others take the matrix cores
+FEW_TOKEN_SHAPES = [(16384, 4096, 2, True), (16384, 4096, 3, False), (16384, 4096, 4, False),
+                    (4096, 16384, 2, True), (4096, 16384, 4, False), (4096, 4096, 4, True),
+                    (1001, 8192, 3, True), (257, 4352, 2, True), (256, 4096, 3, True),
+                    (33, 768, 4, True), (3, 256, 2, True), (4096, 12288, 3, False)]
+
+
+@pytest.mark.parametrize("N,K,M,valu", FEW_TOKEN_SHAPES)
+def test_gemm_few_tokens_equal_gemv(tq2, N, K, M, valu):
+    """2 to 4 tokens on the one-pass VALU matvec (each code word masked once
+    for all tokens): every token's output equals tq2_gemv's on that token bit
+    for bit (fewer rows per wave than tq2_gemv, same per-row sums), and no
+    workspace is needed.  Every route: the oracle's output within the fp16
+    tolerance."""
+    _, c, s, _ = _packed(2600 + N + M, N, K)
+    g = synth.rng(2700 + M)
+    X = np.stack([synth.activations(g, K) for _ in range(M)])
+    dc, ds = _to_dev(c, s)
+    Xd = torch.from_numpy(np.ascontiguousarray(X, np.float16)).to(DEV)
+    need = tq2.tq2_gemm_workspace_bytes(N, K, M)
+    ws = torch.empty(max(256, need), dtype=torch.uint8, device=DEV)
+    Y = tq2.tq2_gemm(dc, ds, Xd, ws=ws)
+    Yv = [tq2.tq2_gemv(dc, ds, Xd[m].contiguous()) for m in range(M)]
+    torch.cuda.synchronize()
+    ref = oracle.gemm(c, s, N, K, synth.bits(X))
+    Yc = Y.cpu().numpy()
+    if valu:
+        assert need == 0
+        for m in range(M):
+            assert torch.equal(Y[m], Yv[m]), (N, K, M, m)
+    for m in range(M):
+        _check_f16(Yc[m], ref[m], _tol(s, X[m], N, K), key=f"gemm few {N}x{K} M={M}")
 
 
 @pytest.mark.parametrize("M", [3, 17])
