@@ -386,6 +386,7 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
     ("c3q down 4096x16384 int8, pre-quantized x_q (tq2_gemv_i8q)", 4096, 16384, "i8q", 1004),
     ("batched gate 16384x4096, 16 tokens per call (tq2_gemm)", 16384, 4096, "gemm16", 1005),
     ("batched gate 16384x4096, 1 token per call (tq2_gemm)", 16384, 4096, "gemm1", 1005),
+    ("batched q/o 4096x4096, 4 tokens per call (tq2_gemm)", 4096, 4096, "gemm4", 1006),
     # the adjacent entry points, each a single call on its own shape
     ("next: fused q/k/v 4096+256+256 x 4096 fp16 (tq2_gemv_fused)", 4096, 4096, "qkv", 1006),
     ("next: fused q/k/v 4096+256+256 x 4096 int8 (tq2_gemv_i8_fused)", 4096, 4096, "qkv_i8", 1006),
@@ -405,7 +406,7 @@ WARM_REPLAYS = 10
 WARM_SECONDS = 0.25
 REQUANT_S_OUT = 0.05
 CPU_TIMED_KINDS = ("f16", "f16_out", "gate_up", "i8", "i8q")
-GEMM_TOKENS = {"gemm16": 16, "gemm1": 1}
+GEMM_TOKENS = {"gemm16": 16, "gemm1": 1, "gemm4": 4}
 
 
 def config_bytes(kind, N, K, rows):
@@ -1200,9 +1201,18 @@ def main():
             rec["trace_us"] = t_us
             rec["trace_pct_of_peak_hbm"] = None if t_us is None else round(
                 100 * rec["bytes_per_call"] / t_us / 1e3 / PEAK_HBM_GBS, 2)
-            if CONFIGS[ci][3] in GEMM_TOKENS and stack is not None:
+            if CONFIGS[ci][3] in GEMM_TOKENS:
+                # against that many one-token calls of the same shape: the
+                # single-call configuration of that shape, or the gate/up
+                # launches of the step for 16384x4096
                 m = GEMM_TOKENS[CONFIGS[ci][3]]
-                rec[f"speedup_vs_{m}_gemv"] = round(m * out["roofline"]["us_per_launch"] / rec["us_per_call"], 2)
+                N_, K_ = CONFIGS[ci][1], CONFIGS[ci][2]
+                one = next((out["configs"][c[0]]["us_per_call"] for c in CONFIGS
+                            if c[3] == "f16" and (c[1], c[2]) == (N_, K_) and c[0] in out["configs"]), None)
+                if one is None and (N_, K_) == (16384, 4096) and stack is not None:
+                    one = out["roofline"]["us_per_launch"]
+                if one is not None:
+                    rec[f"speedup_vs_{m}_gemv"] = round(m * one / rec["us_per_call"], 2)
         c0, c1 = (out["configs"][CONFIGS[i][0]]["us_per_call"] for i in (0, 1))
         qkv = next(out["configs"][c[0]] for c in CONFIGS if c[3] == "qkv")
         qkv["three_single_calls_us"] = round(c1 + 2 * c0, 3)
