@@ -663,17 +663,20 @@ def test_graph_capture_replay(tq2):
     the same calls run eagerly between the replays: every replay equals the
     eager result on the same inputs bit for bit (all kernels are
     deterministic).  Covers the split-K batched path (workspace plus the
-    reduce kernel) and the two-tile batched path."""
+    reduce kernel), the two-tile batched path and the few-token one-pass
+    matvec (2 tokens at 4096x16384, whose LDS needs the raised limit)."""
     (_, ca, sa, _), (_, cb, sb, _), (_, cc, scc, _) = (
         _packed(2300, 256, 4096), _packed(2301, 4096, 16384), _packed(2302, 1000, 1280))
     (dca, dsa), (dcb, dsb), (dcc, dsc) = _to_dev(ca, sa), _to_dev(cb, sb), _to_dev(cc, scc)
     f16 = dict(dtype=torch.float16, device=DEV)
     xa, xb = torch.empty(4096, **f16), torch.empty(16384, **f16)
-    Xb, Xc = torch.empty((20, 16384), **f16), torch.empty((5, 1280), **f16)
+    Xb, Xc, X2 = torch.empty((20, 16384), **f16), torch.empty((5, 1280), **f16), torch.empty((2, 16384), **f16)
     ya, ygu, hh = (torch.empty(256, device=DEV), torch.empty((2, 256), device=DEV),
                    torch.empty(256, device=DEV))
     yi8, Yb, Yc = torch.empty(4096, device=DEV), torch.empty((20, 4096), device=DEV), torch.empty(
         (5, 1000), device=DEV)
+    Y2 = torch.empty((2, 4096), device=DEV)
+    assert tq2.tq2_gemm_workspace_bytes(4096, 16384, 2) == 0  # the one-pass few-token route
     wsb = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(4096, 16384, 20)), dtype=torch.uint8, device=DEV)
     wsc = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(1000, 1280, 5)), dtype=torch.uint8, device=DEV)
     assert tq2.tq2_gemm_workspace_bytes(4096, 16384, 20) > 0  # split K (and two tiles) in the graph
@@ -686,12 +689,13 @@ def test_graph_capture_replay(tq2):
         tq2.tq2_gemv_i8(dcb, dsb, xb, s_in, y=yi8)
         tq2.tq2_gemm(dcb, dsb, Xb, y=Yb, ws=wsb)
         tq2.tq2_gemm(dcc, dsc, Xc, y=Yc, ws=wsc)
+        tq2.tq2_gemm(dcb, dsb, X2, y=Y2)
 
-    outs = [ya, ygu, hh, yi8, Yb, Yc]
+    outs = [ya, ygu, hh, yi8, Yb, Yc, Y2]
 
     def fill(seed):
         g = synth.rng(seed)
-        for t in (xa, xb, Xb, Xc):
+        for t in (xa, xb, Xb, Xc, X2):
             vals = np.stack([synth.activations(g, t.shape[-1]) for _ in range(t.numel() // t.shape[-1])])
             t.copy_(torch.from_numpy(vals.reshape(t.shape)))
 
@@ -709,7 +713,7 @@ def test_graph_capture_replay(tq2):
         got = [o.clone() for o in outs]
         run()
         torch.cuda.synchronize()
-        for name, a, b in zip(["gemv", "gate_up", "silu", "i8", "gemm_splitk_2tile", "gemm"], got, outs):
+        for name, a, b in zip(["gemv", "gate_up", "silu", "i8", "gemm_splitk_2tile", "gemm", "gemm_few"], got, outs):
             assert torch.equal(a, b), (rep, name)
 
 
