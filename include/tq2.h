@@ -231,8 +231,11 @@ size_t tq2_gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);
  * code word once for all M tokens, while the activations it stages over all
  * its workgroups (workgroups x M x 2K bytes) stay within 32 MiB, which
  * holds for small and medium N: no workspace, and every token's output
- * equals tq2_gemv's bit for bit.  Other calls run on the matrix cores.  For M >= 2 a token's output does not depend on the other
- * tokens of the call. */
+ * equals tq2_gemv's bit for bit.  Other calls run on the matrix cores.  A
+ * token's output does not depend on the values of the other tokens of the
+ * call; calls with different M can take different plans (route, K split,
+ * rows per wave), so the same token may differ in its last bits between
+ * them, always within the bound above. */
 #define TQ2_MAX_TOKENS 65536
 int32_t tq2_gemm(const uint8_t *codes, const uint16_t *scales, int64_t N,
                  int64_t K, const uint16_t *x, int64_t M, float *y, void *ws,

@@ -1362,7 +1362,8 @@ GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
   p.U = 4;
   p.mt = (M + kTok - 1) / kTok;
   const int64_t steps = K / kBlock;
-  const int64_t rsets = ((N + kTileRows16 - 1) / kTileRows16 + p.U - 1) / p.U;
+  const int64_t groups = (N + kTileRows16 - 1) / kTileRows16;
+  int64_t rsets = (groups + p.U - 1) / p.U;
   // Two token tiles per wave (one decode of the weights for 32 tokens, one
   // step per load batch to bound the registers) once there are two tiles and
   // the matrix is large (>= 2^26 weights: the gate/up and down shapes).
@@ -1378,6 +1379,23 @@ GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M) {
   // at up to 8 tokens, and every shape loses at 1-2 tokens).  Two-tile waves
   // (more than 16 tokens) always take it.
   p.xl = M > 8 || (M >= 4 && rsets * steps >= 4096);
+  // Row groups per wave: below 64 steps (K < 16384), with one token tile
+  // per wave, the most of 4, 2, 1 that still leaves more row sets than half
+  // the CUs, where K is then not split: the split's partials and second
+  // launch cost more than decoding each step's x for fewer rows (measured
+  // on MI355X, same box: 4096x4096 at 5/16/32 tokens 7.56/8.10/9.20 ->
+  // 5.23/5.86/6.94 us with 1; 4608x4096 at 8 tokens 8.81 -> 7.50 with 2;
+  // 4096x12288 at 8 tokens 19.7 -> 12.3; 256x4096 at 16 tokens 7.84 ->
+  // 6.50 with 1 and the split kept; no case slower).  At 64 steps and more
+  // each CU would decode 4x the x steps for the same rows: 4096x16384 at
+  // 16 tokens 12.4 us with 4 row groups, 13.1 with 2, 15.0 with 1.
+  if (p.TT == 1 && steps < 64) {
+    for (int u = 4; u >= 1; u /= 2) {
+      p.U = u;
+      rsets = (groups + u - 1) / u;
+      if (2 * rsets * p.zt > device_cus()) break;
+    }
+  }
   // Measured on MI355X: when the row sets alone fill the CUs, or K is long
   // (>= 8192), 8 chunk-waves per workgroup with 2 steps per load batch;
   // otherwise (few rows, short K: K is split across workgroups anyway) 4
@@ -1423,6 +1441,24 @@ static bool gemm_on_valu(int64_t N, int64_t K, int64_t M) {
          f16m_staging_bytes(N, K, M) <= kValuStagingBytes;
 }
 
+// One token tile per wave, U row groups: the instantiation for the plan's
+// steps per load batch, chunk-waves and x path.
+template <int U>
+static void launch_gemm_tile(const GemmPlan& p, dim3 grid, hipStream_t st, const GemmArgs& a) {
+  if (p.T == 2 && p.S == 8 && p.xl)
+    hipLaunchKernelGGL((k_gemm_mfma<U, 2, 8, 1, true>), grid, dim3(64 * 8), 0, st, a);
+  else if (p.T == 2 && p.S == 8)
+    hipLaunchKernelGGL((k_gemm_mfma<U, 2, 8, 1, false>), grid, dim3(64 * 8), 0, st, a);
+  else if (p.T == 2 && p.xl)
+    hipLaunchKernelGGL((k_gemm_mfma<U, 2, 4, 1, true>), grid, dim3(64 * 4), 0, st, a);
+  else if (p.T == 2)
+    hipLaunchKernelGGL((k_gemm_mfma<U, 2, 4, 1, false>), grid, dim3(64 * 4), 0, st, a);
+  else if (p.xl)
+    hipLaunchKernelGGL((k_gemm_mfma<U, 1, 4, 1, true>), grid, dim3(64 * 4), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm_mfma<U, 1, 4, 1, false>), grid, dim3(64 * 4), 0, st, a);
+}
+
 size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M) {
   if (M == 1 || gemm_on_valu(N, K, M)) return 0;  // the matvec kernels (see launch_gemm)
   const GemmPlan p = plan_gemm(N, K, M);
@@ -1465,20 +1501,14 @@ hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, 
   a.M = M;
   a.steps_per_split = (int32_t)p.steps_per_split;
   const dim3 grid((unsigned)p.wgs, (unsigned)p.splits, (unsigned)p.zt);
-  if (p.TT == 2)  // implies xl
+  if (p.TT == 2)  // implies xl and 4 row groups
     hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 2, true>), grid, dim3(64 * 4), 0, st, a);
-  else if (p.T == 2 && p.S == 8 && p.xl)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 8, 1, true>), grid, dim3(64 * 8), 0, st, a);
-  else if (p.T == 2 && p.S == 8)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 8, 1, false>), grid, dim3(64 * 8), 0, st, a);
-  else if (p.T == 2 && p.xl)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 4, 1, true>), grid, dim3(64 * 4), 0, st, a);
-  else if (p.T == 2)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 2, 4, 1, false>), grid, dim3(64 * 4), 0, st, a);
-  else if (p.xl)
-    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 1, true>), grid, dim3(64 * 4), 0, st, a);
+  else if (p.U == 4)
+    launch_gemm_tile<4>(p, grid, st, a);
+  else if (p.U == 2)
+    launch_gemm_tile<2>(p, grid, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_mfma<4, 1, 4, 1, false>), grid, dim3(64 * 4), 0, st, a);
+    launch_gemm_tile<1>(p, grid, st, a);
   if (p.splits > 1) {
     const int64_t MN = M * N;
     hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, part,

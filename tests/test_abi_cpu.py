@@ -165,7 +165,7 @@ def test_error_paths_fused_and_epilogues(tq2):
 @no_gpu
 def test_error_paths_gemm(tq2):
     lib = tq2.lib()
-    N, K, M = 4096, 4096, 16
+    N, K, M = 256, 4096, 16  # K split: a workspace is needed
     need = lib.tq2_gemm_workspace_bytes(N, K, M)
     assert 0 < need < 2 ** 40
     assert lib.tq2_gemm_workspace_bytes(N, 1000, M) == ctypes.c_size_t(-1).value
@@ -185,10 +185,14 @@ def test_error_paths_gemm(tq2):
 
 @no_gpu
 def test_gemm_workspace_only_for_split_k(tq2):
-    """The 16384-row shapes run without a K split (no workspace); small N
-    splits K and needs the partials."""
+    """The 16384-row shapes run without a K split (no workspace), and so do
+    4096 rows below K = 16384 (one row group per wave); 256 rows, and 4096
+    rows at K = 16384, split K and need the partials."""
     lib = tq2.lib()
     assert lib.tq2_gemm_workspace_bytes(16384, 4096, 16) == 0
+    assert lib.tq2_gemm_workspace_bytes(4096, 4096, 16) == 0
+    assert lib.tq2_gemm_workspace_bytes(4096, 12288, 8) == 0
+    assert lib.tq2_gemm_workspace_bytes(4096, 16384, 16) == 4 * 16 * 4096 * 4
     assert lib.tq2_gemm_workspace_bytes(256, 4096, 16) % (4 * 16 * 256) == 0
     assert lib.tq2_gemm_workspace_bytes(256, 4096, 16) > 0
 
@@ -208,7 +212,9 @@ def test_gemm_few_tokens_need_no_workspace(tq2):
 @no_gpu
 def test_gemm_split_rule(tq2):
     """K is split only while the workgroups still fit one per CU (256 CUs):
-    the workspace is splits x M x N fp32 partials, or 0 without a split."""
+    the workspace is splits x M x N fp32 partials, or 0 without a split.
+    Below K = 16384 a wave takes 4, 2 or 1 row groups, the most that leave
+    more workgroups than half the CUs, so medium N runs unsplit."""
     lib = tq2.lib()
     ws = lib.tq2_gemm_workspace_bytes
     assert ws(16384, 4096, 32) == 0                 # 256 row sets, two tiles per wave
@@ -217,8 +223,11 @@ def test_gemm_split_rule(tq2):
     assert ws(4096, 16384, 16) == 4 * 16 * 4096 * 4  # 64 row sets -> 4 splits
     assert ws(4096, 16384, 32) == 4 * 32 * 4096 * 4
     assert ws(4096, 16384, 48) == 2 * 48 * 4096 * 4  # 128 workgroups -> 2 splits
-    assert ws(4096, 4096, 16) == 4 * 16 * 4096 * 4   # 64 -> 4 (every wave keeps its step)
-    assert ws(4096, 4096, 32) == 2 * 32 * 4096 * 4   # 128 -> 2
+    assert ws(4096, 4096, 16) == 0                   # 1 row group per wave: 256 row sets
+    assert ws(4096, 4096, 32) == 0                   # 2 per wave: 128 row sets x 2 tiles
+    assert ws(4608, 4096, 8) == 0                    # 2 per wave: 144 row sets
+    assert ws(1024, 4096, 16) == 4 * 16 * 1024 * 4   # 1 per wave: 64 row sets -> 4 splits
+    assert ws(256, 4096, 16) == 4 * 16 * 256 * 4     # 16 row sets -> 4 (every wave keeps its step)
 
 
 def test_noalloc_scratch_covers_every_split(tq2):

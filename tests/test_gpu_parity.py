@@ -552,7 +552,10 @@ GEMM_SHAPES = [(256, 4096, 16), (33, 768, 5), (4096, 4096, 2), (1000, 1280, 17),
                (4096, 16384, 16), (16384, 4096, 8), (7, 65280, 3), (300, 4352, 33),
                (4096, 16384, 20), (16384, 4096, 40),
                (16384, 4096, 4),   # fewest tokens that stage x through LDS on a large shape
-               (300, 4352, 100)]   # seven token tiles, the last one ragged
+               (300, 4352, 100),   # seven token tiles, the last one ragged
+               # fewer row groups per wave below 16384 columns: 2 per wave, K unsplit;
+               # 1 per wave over 3 and 2 load batches; 1 per wave, K split in 4, ragged N
+               (4608, 4096, 8), (4096, 12288, 8), (4096, 8192, 16), (1001, 4096, 7)]
 
 
 @pytest.mark.parametrize("N,K,M", GEMM_SHAPES)
@@ -573,14 +576,15 @@ def test_gemm_parity(tq2, N, K, M):
         _check_f16(Yc[m], ref[m], _tol(s, X[m], N, K), key=f"gemm {N}x{K} M={M}")
 
 
-def test_gemm_token_independence_and_determinism(tq2):
+@pytest.mark.parametrize("N,K", [(4096, 16384), (4096, 4096)])
+def test_gemm_token_independence_and_determinism(tq2, N, K):
     """A token's output does not depend on the other tokens of the call, and
     repeated calls are bitwise identical (split partials added in order).
     16 tokens (matrix cores) and 5 tokens (matrix cores, x loaded per lane)
     give the same bits for a token; 1 and 2 tokens run the VALU matvec
     kernels, bit-equal to tq2_gemv, and within the fp16 tolerance of the
-    matrix-core result."""
-    N, K = 4096, 16384
+    matrix-core result.  4096x16384 runs 4 row groups per wave with K split
+    in 4; 4096x4096 one row group per wave, K unsplit."""
     _, c, s, _ = _packed(1950, N, K)
     g = synth.rng(1951)
     X = np.stack([synth.activations(g, K) for _ in range(16)])
