@@ -387,6 +387,7 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
     ("batched gate 16384x4096, 16 tokens per call (tq2_gemm)", 16384, 4096, "gemm16", 1005),
     ("batched gate 16384x4096, 1 token per call (tq2_gemm)", 16384, 4096, "gemm1", 1005),
     ("batched q/o 4096x4096, 4 tokens per call (tq2_gemm)", 4096, 4096, "gemm4", 1006),
+    ("batched q/o 4096x4096, 16 tokens per call (tq2_gemm)", 4096, 4096, "gemm16", 1007),
     # the adjacent entry points, each a single call on its own shape
     ("next: fused q/k/v 4096+256+256 x 4096 fp16 (tq2_gemv_fused)", 4096, 4096, "qkv", 1006),
     ("next: fused q/k/v 4096+256+256 x 4096 int8 (tq2_gemv_i8_fused)", 4096, 4096, "qkv_i8", 1006),
