@@ -71,6 +71,7 @@ STEP_SEEDS = {"weights": "10000 + 7*layer + proj", "x": "20000 + 7*layer + proj"
 
 # trace-marker ids (workgroups of the empty marker kernel) of the timed sections
 MARK_STEP, MARK_DOMINANT, MARK_FUSED, MARK_FLOOR, MARK_SWEEP, MARK_END = 1, 2, 3, 4, 5, 6
+MARK_DOMINANT_PROBE = 7
 MARK_CONFIG, MARK_CONFIG_PROBE = 100, 200  # + index of the configuration
 
 
@@ -1106,7 +1107,8 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f16", "accumulate": "f32", "data": "synthetic"}
-    markers = {MARK_STEP: "decode step", MARK_DOMINANT: "dominant kernel", MARK_FUSED: "step_fused",
+    markers = {MARK_STEP: "decode step", MARK_DOMINANT: "dominant kernel",
+               MARK_DOMINANT_PROBE: "read probe: dominant kernel", MARK_FUSED: "step_fused",
                MARK_FLOOR: "dispatch floor", MARK_SWEEP: "read probe sweep", MARK_END: None}
     for ci, c in enumerate(CONFIGS):
         markers[MARK_CONFIG + ci] = c[0]
@@ -1147,6 +1149,12 @@ def main():
         dom_bytes = sum(algo_bytes(e["N"], e["K"]) for e in dom) / len(dom)
         achieved = dom_bytes / us_dom / 1e3
         us_tr, kname = trace_kernel_us(trace, markers[MARK_DOMINANT])
+        # the read-only stream of the same weight bytes per launch, over as
+        # many distinct buffers as the launches (the same rotation), timed the
+        # same way: the achievable ceiling of one dispatch of this size
+        de = dom[0]
+        rb = (de["N"] * de["K"] * 66 // 256 + 255) // 256 * 256
+        us_rd = read_ceiling(torch, probes, rb, len(dom), 10, READ_CEILING, MARK_DOMINANT_PROBE)
         roofline = {"bound": "hbm", "kernel": DOMINANT_KERNEL,
                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(sha),
@@ -1154,6 +1162,7 @@ def main():
                     "launches_timed": len(dom), "kernel_source_sha": sha,
                     "us_per_launch_trace": us_tr,
                     "frac_trace": None if us_tr is None else round(dom_bytes / us_tr / 1e3 / PEAK_HBM_GBS, 4),
+                    "read_probe_us": round(us_rd, 3), "frac_of_read_probe": round(us_rd / us_dom, 4),
                     "gates": "frac (HIP events over the 64 gate/up launches of one step replayed back to back: "
                              "the decode stream's view); frac_trace is the committed rocprofv3 kernel trace of "
                              "the same section on this kernel source (kernel begin to end, under the tracer)"}
