@@ -576,6 +576,49 @@ def test_gemm_parity(tq2, N, K, M):
         _check_f16(Yc[m], ref[m], _tol(s, X[m], N, K), key=f"gemm {N}x{K} M={M}")
 
 
+def _gemm_sweep_cases(seed=7):
+    """Seeded shapes for the batched planner, one per (N range, M range):
+    N in 1..300, 1000..6000 or 8000..20000; M = 1, 2..4, 5..16 or 17..40;
+    K a multiple of 256 up to 64 blocks; N*K <= 2^26 and N*K*M <= 2^30, so
+    that the oracle finishes in seconds.  With this seed the plans include
+    the one-token kernel, the one-pass few-token matvec, the matrix cores
+    with 1, 2 and 4 row groups per wave, K split and unsplit, one and two
+    steps per load batch, x through LDS and through registers."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for nlo, nhi in ((1, 300), (1000, 6000), (8000, 20000)):
+        for mlo, mhi in ((1, 1), (2, 4), (5, 16), (17, 40)):
+            while True:
+                N, K = int(g.integers(nlo, nhi + 1)), 256 * int(g.integers(1, 65))
+                M = int(g.integers(mlo, mhi + 1))
+                if N * K <= 1 << 26 and N * K * M <= 1 << 30:
+                    break
+            cases.append((N, K, M))
+    return cases
+
+
+@pytest.mark.parametrize("N,K,M", _gemm_sweep_cases())
+def test_gemm_plan_sweep(tq2, N, K, M):
+    """Random shapes and token counts through every route of the batched
+    planner (one-token kernel, one-pass few-token matvec, matrix cores with
+    1, 2 or 4 row groups per wave, K split or not, one or two token tiles,
+    x through LDS or registers) against the oracle, and a repeated call
+    bitwise identical."""
+    _, c, s, _ = _packed(5000 + N + M, N, K)
+    g = synth.rng(5100 + M)
+    X = np.stack([synth.activations(g, K) for _ in range(M)])
+    dc, ds = _to_dev(c, s)
+    Xd = torch.from_numpy(np.ascontiguousarray(X, np.float16)).to(DEV)
+    Y = tq2.tq2_gemm(dc, ds, Xd)
+    Y2 = tq2.tq2_gemm(dc, ds, Xd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    ref = oracle.gemm(c, s, N, K, synth.bits(X))
+    Yc = Y.cpu().numpy()
+    for m in range(M):
+        _check_f16(Yc[m], ref[m], _tol(s, X[m], N, K), key=f"gemm sweep {N}x{K} M={M}")
+
+
 @pytest.mark.parametrize("N,K", [(4096, 16384), (4096, 4096)])
 def test_gemm_token_independence_and_determinism(tq2, N, K):
     """A token's output does not depend on the other tokens of the call, and
