@@ -430,6 +430,40 @@ def test_gemv_i8_bit_exact(tq2, N, K, div):
     assert np.array_equal(y2.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
 
 
+def _matvec_sweep_cases(seed=11):
+    """Seeded one-token shapes: N in 1..300, 300..6000 or 6000..40000, K a
+    multiple of 256 up to 255 blocks (the int8 path's limit), N*K <= 2^27.
+    With this seed: 1, 2, 3, 5 and 12 chunks of 4096 (the run-time chunk
+    kernels among them), full and partial last chunks, 2, 4 and 8 rows per
+    wave, ragged row groups."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for nlo, nhi in ((1, 300), (300, 6000), (6000, 40000)):
+        for kb in ((1, 16), (17, 64), (65, 255)):
+            while True:
+                N, K = int(g.integers(nlo, nhi + 1)), 256 * int(g.integers(kb[0], kb[1] + 1))
+                if N * K <= 1 << 27:
+                    break
+            cases.append((N, K))
+    return cases
+
+
+@pytest.mark.parametrize("N,K", _matvec_sweep_cases())
+def test_matvec_shape_sweep(tq2, N, K):
+    """Seeded shapes through tq2_gemv (the fp16 bound and the kernel's own
+    bound) and tq2_gemv_i8 (bit-exact: codes, partial sums, outputs)."""
+    q, codes, scales, x = _packed(6000 + N, N, K)
+    c, sc, xd = _to_dev(codes, scales, x)
+    y = tq2.tq2_gemv(c, sc, xd)
+    s = np.float32(np.float32(np.abs(x.astype(np.float32)).max()) / np.float32(100))
+    yi = tq2.tq2_gemv_i8(c, sc, xd, s)
+    torch.cuda.synchronize()
+    _check_gemv(y.cpu().numpy(), oracle.gemv(codes, scales, N, K, synth.bits(x)), scales, x, N, K,
+                f"gemv sweep {N}x{K}")
+    yi_ref, _ = oracle.gemv_i8q(codes, scales, N, K, oracle.quantize_i8(synth.bits(x), s), s)
+    assert np.array_equal(yi.cpu().numpy().view(np.uint32), yi_ref.view(np.uint32))
+
+
 def test_gemv_i8_extreme_scales_and_one_hot(tq2):
     N, K = 5, 512
     q, codes, scales, _ = _packed(950, N, K)
