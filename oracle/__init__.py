@@ -15,6 +15,7 @@ Functions (each cites its passage in tq2_oracle.c):
   requant_i8(y, s_out)         -> y_q, y_deq
   silu_mul(g, u)               -> h (fp64)
   gemm(codes, scales, N, K, X_bits[M][K]) -> Y[M][N] (one matvec per token)
+  gemm_i8q(codes, scales, N, K, XQ[M][K], s) -> Y[M][N] (one int8 matvec per token)
   half_to_float(bits), float_to_half(value)
   threads(), set_threads(n)
 """
@@ -199,3 +200,15 @@ def gemm(codes, scales, N, K, X_bits):
     Y = np.empty((M, N), np.float32)
     _lib().oracle_gemm(pc, ps, N, K, px, M, Y.ctypes.data_as(ctypes.c_void_p))
     return Y
+
+
+def gemm_i8q(codes, scales, N, K, XQ, s):
+    """The int8 matvec (gemv_i8q: page "gemma4 wNa8o8 requires int8
+    activations", Implemented section) for each of M tokens of pre-quantized
+    activations XQ[M][K] sharing the activation scale s; Y[M][N] fp32."""
+    _shape_check(N, K)
+    XQ = np.ascontiguousarray(XQ, np.int8)
+    M = XQ.size // K
+    assert XQ.size == M * K and M >= 1
+    return np.stack([gemv_i8q(codes, scales, N, K, XQ.reshape(M, K)[m], s)[0] for m in range(M)])
+

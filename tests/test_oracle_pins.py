@@ -341,6 +341,25 @@ def test_int8_brute_force(N, K, seed, div):
     assert np.array_equal(oracle.gemv_i8(codes, sc, N, K, synth.bits(x), s), y)
 
 
+def test_gemm_i8q_brute_force_tokens():
+    """Batched int8 oracle: every token's row bit-exact against the exact
+    integer computation, and a token's output independent of the others."""
+    N, K, M = 3, 768, 5
+    q, d, _ = synth.problem(43, N, K)
+    g = synth.rng(44)
+    X = np.stack([synth.activations(g, K) for _ in range(M)])
+    s = np.float32(np.float32(np.abs(X.astype(np.float32)).max()) / np.float32(100))
+    XQ = np.stack([oracle.quantize_i8(synth.bits(X[m]), s) for m in range(M)])
+    codes = _fields_to_bytes(q)
+    sc = synth.bits(d).reshape(N, K // 256)
+    Y = oracle.gemm_i8q(codes, sc, N, K, XQ, s)
+    assert Y.shape == (M, N) and Y.dtype == np.float32
+    for m in range(M):
+        assert np.array_equal(Y[m], brute.exact_i8_y(q, synth.bits(d), XQ[m], s))
+    perm = [4, 2, 0, 3, 1]
+    assert np.array_equal(oracle.gemm_i8q(codes, sc, N, K, XQ[perm], s), Y[perm])
+
+
 def test_int8_large_scales_exact():
     """Scales near the top of binary16 exercise the full D = d*2^24 range."""
     N, K = 2, 512
