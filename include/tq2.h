@@ -241,6 +241,33 @@ int32_t tq2_gemm(const uint8_t *codes, const uint16_t *scales, int64_t N,
                  int64_t K, const uint16_t *x, int64_t M, float *y, void *ws,
                  size_t ws_bytes, tq2_stream_t stream);
 
+/* tq2_gemm_i8q_workspace_bytes -- device workspace that tq2_gemm_i8q
+ * needs: the split sums (8*M*N bytes per split, int64) when the plan splits
+ * K across workgroups, which it does only when N gives too few row groups
+ * to fill the GPU; 0 otherwise, and 0 for M = 1.  (size_t)-1 for an
+ * invalid shape or token count. */
+size_t tq2_gemm_i8q_workspace_bytes(int64_t N, int64_t K, int64_t M);
+
+/* tq2_gemm_i8q -- the int8 matvec of page "gemma4 wNa8o8 requires int8
+ * activations" (Implemented section), tq2_gemv_i8q's, for M tokens at once:
+ * x_q [M][K] int8 activations (row-major, 16-byte aligned, already
+ * quantized with the activation scale s, for example by tq2_quantize_i8 on
+ * each token), Y [M][N] fp32 (row-major).  Row n of token m equals
+ * tq2_gemv_i8q(W, x_q[m], s) bit for bit: every 256-block's sum of
+ * x_q * (code - 1) is exact (int32 on the matrix cores), the blocks are
+ * scaled and summed exactly in int64, and the same epilogue
+ * fp32(fp64(A) * s * 2^-24) follows.  1 <= M <= TQ2_MAX_TOKENS, K <=
+ * TQ2_I8_MAX_K, s finite and > 0 (TQ2_ERR_SCALE).  ws: when
+ * tq2_gemm_i8q_workspace_bytes(N, K, M) is non-zero, device memory of at
+ * least that many bytes, 256-byte aligned, not overlapping x_q or Y
+ * (TQ2_ERR_WORKSPACE otherwise); its contents on entry do not matter.
+ * Otherwise ws may be NULL.  One kernel on `stream` (two when K is split);
+ * M = 1 runs tq2_gemv_i8q's kernel.  The weights are streamed once for all
+ * M tokens. */
+int32_t tq2_gemm_i8q(const uint8_t *codes, const uint16_t *scales, int64_t N,
+                     int64_t K, const int8_t *x_q, int64_t M, float s, float *y,
+                     void *ws, size_t ws_bytes, tq2_stream_t stream);
+
 /* tq2_gemm_noalloc -- tq2_gemm for callers that cannot allocate (code
  * under HIP graph capture, serving loops or harnesses that forbid
  * hipMalloc): the same kernels and results (bit-identical to tq2_gemm), but

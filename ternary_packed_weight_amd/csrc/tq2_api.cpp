@@ -322,6 +322,31 @@ int32_t tq2_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_
   return hip_status(tq2::launch_gemm(codes, scales, N, K, x, M, y, ws, (hipStream_t)stream));
 }
 
+size_t tq2_gemm_i8q_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+  if (check_shape(N, K, TQ2_I8_MAX_K) != TQ2_OK || M < 1 || M > TQ2_MAX_TOKENS) return (size_t)-1;
+  return tq2::gemm_i8_workspace_bytes(N, K, M);
+}
+
+int32_t tq2_gemm_i8q(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const int8_t* x_q,
+                     int64_t M, float s, float* y, void* ws, size_t ws_bytes, tq2_stream_t stream) {
+  TQ2_TRY(check_shape(N, K, TQ2_I8_MAX_K));
+  TQ2_TRY(check_weights(codes, scales));
+  if (M < 1 || M > TQ2_MAX_TOKENS || !x_q || !y) return TQ2_ERR_ARG;
+  if (M * N > ((int64_t)1 << 40)) return TQ2_ERR_SHAPE;
+  if (!aligned(x_q, 16) || !aligned(y, 4)) return TQ2_ERR_ALIGN;
+  TQ2_TRY(check_scale(s));
+  const size_t xb = (size_t)(M * K), yb = (size_t)(M * N) * 4;
+  const size_t cb = (size_t)(N * (K / 4)), sb = (size_t)(N * (K / TQ2_BLOCK)) * 2;
+  if (overlaps(y, yb, x_q, xb) || overlaps(y, yb, codes, cb) || overlaps(y, yb, scales, sb)) return TQ2_ERR_ARG;
+  const size_t need = tq2::gemm_i8_workspace_bytes(N, K, M);
+  if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return TQ2_ERR_WORKSPACE;
+  if (need && (overlaps(ws, need, x_q, xb) || overlaps(ws, need, y, yb) || overlaps(ws, need, codes, cb) ||
+               overlaps(ws, need, scales, sb)))
+    return TQ2_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return hip_status(tq2::launch_gemm_i8(codes, scales, N, K, x_q, M, s, y, ws, (hipStream_t)stream));
+}
+
 int32_t tq2_gemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                          const uint16_t* x, int64_t M, float* y, tq2_stream_t stream) {
   TQ2_TRY(gemm_args(codes, scales, N, K, x, M, y));

@@ -60,6 +60,10 @@ struct GemmPlan {
   int64_t part_bytes;
 };
 GemmPlan plan_gemm(int64_t N, int64_t K, int64_t M);
+GemmPlan plan_gemm_i8(int64_t N, int64_t K, int64_t M);
+size_t gemm_i8_workspace_bytes(int64_t N, int64_t K, int64_t M);
+hipError_t launch_gemm_i8(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                          const int8_t* xq, int64_t M, float s, float* y, void* ws, hipStream_t st);
 size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M);
 hipError_t launch_gemm(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                        const uint16_t* x, int64_t M, float* y, void* ws, hipStream_t st);

@@ -1959,6 +1959,304 @@ hipError_t launch_gemv_i8_requant(const MatSet& m, int64_t K, const uint16_t* x,
   }
 }
 
+// ------------------------------------- small-M batched int8 matvec (MFMA)
+//
+// Y[M][N] for M tokens of int8 activations x_q sharing the scale s: per
+// token the int8 matvec of tq2_gemv_i8q (page "gemma4 wNa8o8 requires int8
+// activations", Implemented section), with each 256-block's exact sum
+// P = sum_k x_q(k) (q(k) - 1) formed on the matrix cores
+// (v_mfma_i32_16x16x64_i8: 16 rows x 16 tokens x 64 k, int32 exact), then
+// the same exact A = sum_b (d_b 2^24) P_b in int64 and the same epilogue.
+// Integer sums give the same A in any order, so every token's output equals
+// tq2_gemv_i8q's bit for bit.
+//
+// Operands.  Lane (G = l/16, i = l%16) loads row i's 16 code bytes of block
+// quarter G (codes k = 64G + 4b + f of the block in byte b, bit pair f).
+// (v >> 2f) & 0x03030303 puts the 16 codes k = 64G + 4b + f (b = 0..15) in
+// 16 bytes, the A operand of MFMA f; its B operand is token i's x_q at the
+// same k: byte f of each of the lane's 16 x_q dwords, gathered by a 4 x 4
+// byte transpose of every 4 dwords.  A and B put the same k in the same lane
+// group and byte, so each MFMA sums the block's k = f mod 4 (the order inside
+// the instruction is the hardware's and does not matter for integers).
+// D: lane (G, i) gets rows 4G..4G+3 of token i.  The zero point sum_k x_q
+// is the lane's 64 bytes (4 v_dot4 per 16) summed over its lane group.
+
+struct GemmI8Args {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const int8_t* xq;  // X_q[M][K]
+  float s;
+  float* y;          // y[M][N] (no split)
+  int64_t* part;     // the split sums A [splits][M][N] (split K)
+  int64_t N, K, M;
+  int32_t steps_per_split;  // multiple of C*T
+};
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// byte f of a, b, c, d as the dword {a_f, b_f, c_f, d_f}, for f = 0..3
+__device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                                   uint32_t (&o)[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const uint32_t t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  const uint32_t t2 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  const uint32_t t3 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
+  o[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// Workgroup: C waves, the C chunks of steps of one K-split of one row set
+// (U row groups of 16) for one tile of 16 tokens; their int64 sums meet in
+// LDS.  Grid: (row sets, K-splits, token tiles).
+template <int U, int T, int C>
+__global__ __launch_bounds__(64 * C) void k_gemm_i8(GemmI8Args a) {
+  __shared__ int64_t red[C][U][4][64];
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4, i = lane & 15;
+  const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rset = blockIdx.x;
+  const int split = blockIdx.y, tile = blockIdx.z;
+  const int64_t row_bytes = a.K / 4, BK = a.K / kBlock;
+  const int spw = a.steps_per_split / C;  // steps per wave
+  const int s_begin = split * a.steps_per_split + c * spw;
+  const int s_lim = s_begin + spw;
+  const int s_end = (int64_t)s_lim < BK ? s_lim : (int)BK;
+
+  // per row group: scalar descriptors over its valid rows (zeros past N)
+  __amdgpu_buffer_rsrc_t rc[U], rs[U];
+  int valid[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int gi = rset * U + u;
+    int v = (int)(a.N - (int64_t)gi * kTileRows16);
+    v = v < 0 ? 0 : (v > kTileRows16 ? kTileRows16 : v);
+    v = __builtin_amdgcn_readfirstlane(v);
+    valid[u] = v;
+    const int64_t r0 = v > 0 ? (int64_t)gi * kTileRows16 : 0;
+    rc[u] = rsrc(a.codes + r0 * row_bytes, (uint32_t)(v * row_bytes));
+    rs[u] = rsrc(a.scales + r0 * BK, (uint32_t)(v * BK * 2));
+  }
+  // this tile's tokens (past M: zeros, nothing stored)
+  int64_t tv = a.M - (int64_t)tile * kTok;
+  tv = tv > kTok ? kTok : (tv < 0 ? 0 : tv);
+  const __amdgpu_buffer_rsrc_t xr =
+      rsrc(a.xq + (tv > 0 ? (int64_t)tile * kTok * a.K : 0), (uint32_t)(tv * a.K));
+
+  int64_t acc[U][4];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[u][r] = 0;
+
+  for (int s0 = s_begin; s0 < s_end; s0 += T) {
+    // issue, in this order (loads complete in issue order): this lane's 64
+    // x_q bytes of each step (L2), the code words (HBM), the scales
+    uint4 xv[T][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int s = s0 + t < s_end ? s0 + t : s0;  // in range
+      const int xoff = (int)(i * a.K + 256 * (int64_t)s + 64 * G);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) xv[t][n] = load_b128(xr, xoff + 16 * n);
+    }
+    uint4 w[T][U];
+    uint16_t d[T][U][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const bool ok = s0 + t < s_end;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t off = ok ? (uint32_t)(i * row_bytes + 64 * (s0 + t) + 16 * G) : 0x7FFFFFF0u;
+        const v4u v = __builtin_bit_cast(
+            v4u, __builtin_amdgcn_raw_buffer_load_b128(rc[u], (int)off, 0, kNonTemporal));
+        w[t][u] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const bool ok = s0 + t < s_end;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t so = ok ? (uint32_t)(((4 * G + r) * BK + s0 + t) * 2) : 0x7FFFFFF0u;
+          d[t][u][r] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs[u], (int)so, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (s0 + t >= s_end) break;  // uniform
+      const uint32_t xw[16] = {xv[t][0].x, xv[t][0].y, xv[t][0].z, xv[t][0].w,
+                               xv[t][1].x, xv[t][1].y, xv[t][1].z, xv[t][1].w,
+                               xv[t][2].x, xv[t][2].y, xv[t][2].z, xv[t][2].w,
+                               xv[t][3].x, xv[t][3].y, xv[t][3].z, xv[t][3].w};
+      // B operands (one per bit pair f) and the block's sum of x_q for token i
+      uint32_t bo[4][4];
+      int zx = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t o[4];
+        transpose4x4_bytes(xw[4 * e], xw[4 * e + 1], xw[4 * e + 2], xw[4 * e + 3], o);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) bo[f][e] = o[f];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) zx = dot4(xw[4 * e + n], 0x01010101u, zx);
+      }
+      zx += __shfl_xor(zx, 16, 64);
+      zx += __shfl_xor(zx, 32, 64);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t v[4] = {w[t][u].x, w[t][u].y, w[t][u].z, w[t][u].w};
+        v4i D = {0, 0, 0, 0};
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const v4i av = {(int)((v[0] >> (2 * f)) & 0x03030303u), (int)((v[1] >> (2 * f)) & 0x03030303u),
+                          (int)((v[2] >> (2 * f)) & 0x03030303u), (int)((v[3] >> (2 * f)) & 0x03030303u)};
+          const v4i bv = {(int)bo[f][0], (int)bo[f][1], (int)bo[f][2], (int)bo[f][3]};
+          D = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, D, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[u][r] += scaled_partial(d[t][u][r], D[r] - zx);
+      }
+    }
+  }
+
+  // chunk sums meet in LDS (int64: exact in any order); wave 0 stores
+  if (C > 1) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[c][u][r][lane] = acc[u][r];
+    __syncthreads();
+    if (c != 0) return;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // rolled: unrolled, every chunk's value would be loaded at once
+        int64_t sum = red[0][u][r][lane];
+#pragma unroll 1
+        for (int cc = 1; cc < C; ++cc) sum += red[cc][u][r][lane];
+        acc[u][r] = sum;
+      }
+  }
+  // lane (G, i): rows 4G..4G+3 of each group, token tile*16 + i
+  const int64_t tok = (int64_t)tile * kTok + i;
+  if (tok >= a.M) return;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t gi = (int64_t)rset * U + u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (4 * G + r >= valid[u]) continue;
+      const int64_t n = gi * kTileRows16 + 4 * G + r;
+      if (a.part) a.part[((int64_t)split * a.M + tok) * a.N + n] = acc[u][r];
+      else a.y[tok * a.N + n] = i8_epilogue(acc[u][r], a.s);
+    }
+  }
+}
+
+// y = the epilogue of the sum over splits of the int64 partials
+__global__ __launch_bounds__(256) void k_gemm_i8_reduce(const int64_t* __restrict__ part, int splits,
+                                                        int64_t MN, float s, float* __restrict__ y) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= MN) return;
+  int64_t A = part[id];
+  for (int p = 1; p < splits; ++p) A += part[(int64_t)p * MN + id];
+  y[id] = i8_epilogue(A, s);
+}
+
+GemmPlan plan_gemm_i8(int64_t N, int64_t K, int64_t M) {
+  GemmPlan p;
+  p.TT = 1;
+  p.xl = false;
+  p.mt = (M + kTok - 1) / kTok;
+  p.zt = p.mt;
+  const int64_t steps = K / kBlock;
+  const int64_t groups = (N + kTileRows16 - 1) / kTileRows16;
+  // row groups per wave: the most of 4, 2, 1 that still leaves more row
+  // sets than half the CUs (building a step's B operands costs ~50
+  // instructions, a row group's decode ~30, so fewer rows per wave cost
+  // little and spare the split)
+  int64_t rsets = groups;
+  for (int u = 4; u >= 1; u /= 2) {
+    p.U = u;
+    rsets = (groups + u - 1) / u;
+    if (2 * rsets * p.zt > device_cus()) break;
+  }
+  const bool wide = rsets * p.zt >= device_cus() || steps >= 32;
+  p.T = wide ? 2 : 1;
+  p.S = (wide && steps >= 16) ? 8 : 4;
+  const int64_t per_split = (int64_t)p.S * p.T;
+  int64_t max_splits = steps / per_split;
+  if (max_splits < 1) max_splits = 1;
+  int64_t splits = 1;
+  while (splits * 2 <= max_splits && rsets * p.zt * splits * 2 <= device_cus()) splits *= 2;
+  int64_t sps = (steps + splits - 1) / splits;
+  sps = (sps + per_split - 1) / per_split * per_split;
+  p.splits = (steps + sps - 1) / sps;
+  p.steps_per_split = sps;
+  p.wgs = rsets;
+  p.part_bytes = p.splits > 1 ? p.splits * M * N * 8 : 0;
+  return p;
+}
+
+size_t gemm_i8_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+  if (M == 1) return 0;  // the one-token int8 kernel (see launch_gemm_i8)
+  return (size_t)plan_gemm_i8(N, K, M).part_bytes;
+}
+
+template <int U>
+static void launch_gemm_i8_tile(const GemmPlan& p, dim3 grid, hipStream_t st, const GemmI8Args& a) {
+  if (p.T == 2 && p.S == 8)
+    hipLaunchKernelGGL((k_gemm_i8<U, 2, 8>), grid, dim3(64 * 8), 0, st, a);
+  else if (p.T == 2)
+    hipLaunchKernelGGL((k_gemm_i8<U, 2, 4>), grid, dim3(64 * 4), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm_i8<U, 1, 4>), grid, dim3(64 * 4), 0, st, a);
+}
+
+hipError_t launch_gemm_i8(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                          const int8_t* xq, int64_t M, float s, float* y, void* ws, hipStream_t st) {
+  if (M == 1) {
+    // one token: the int8 matvec kernel itself (its output, bit for bit)
+    MatSet m{};
+    m.codes[0] = codes;
+    m.scales[0] = scales;
+    m.nmat = 1;
+    m.rows = (int32_t)N;
+    return launch_gemv_i8(m, K, nullptr, xq, s, y, nullptr, st);
+  }
+  const GemmPlan p = plan_gemm_i8(N, K, M);
+  GemmI8Args a;
+  a.codes = codes;
+  a.scales = scales;
+  a.xq = xq;
+  a.s = s;
+  a.y = y;
+  a.part = p.splits > 1 ? static_cast<int64_t*>(ws) : nullptr;
+  a.N = N;
+  a.K = K;
+  a.M = M;
+  a.steps_per_split = (int32_t)p.steps_per_split;
+  const dim3 grid((unsigned)p.wgs, (unsigned)p.splits, (unsigned)p.zt);
+  if (p.U == 4)
+    launch_gemm_i8_tile<4>(p, grid, st, a);
+  else if (p.U == 2)
+    launch_gemm_i8_tile<2>(p, grid, st, a);
+  else
+    launch_gemm_i8_tile<1>(p, grid, st, a);
+  if (p.splits > 1) {
+    const int64_t MN = M * N;
+    hipLaunchKernelGGL(k_gemm_i8_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, a.part,
+                       (int)p.splits, MN, s, y);
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------- static scratch (no allocation)
 // For callers that cannot allocate (graph capture, serving loops that forbid
 // hipMalloc): tq2_gemm's split partials live in this file-scope device array

@@ -65,6 +65,10 @@ _lib.tq2_gemm.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]
 _lib.tq2_gemm.restype = _I32
 _lib.tq2_gemm_noalloc.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P]
 _lib.tq2_gemm_noalloc.restype = _I32
+_lib.tq2_gemm_i8q_workspace_bytes.argtypes = [_I64, _I64, _I64]
+_lib.tq2_gemm_i8q_workspace_bytes.restype = _SZ
+_lib.tq2_gemm_i8q.argtypes = [_P, _P, _I64, _I64, _P, _I64, _F, _P, _P, _SZ, _P]
+_lib.tq2_gemm_i8q.restype = _I32
 
 TQ2_OK = 0
 TQ2_OP_GEMV, TQ2_OP_GATE_UP, TQ2_OP_GEMV_I8, TQ2_OP_GEMV_I8Q = 0, 1, 2, 3
@@ -72,7 +76,7 @@ EXPORTED = ("tq2_abi_version", "tq2_status_string", "tq2_codes_bytes", "tq2_scal
             "tq2_workspace_bytes", "tq2_pack", "tq2_dequant", "tq2_gemv", "tq2_gemv_gate_up",
             "tq2_quantize_i8", "tq2_gemv_i8q", "tq2_gemv_i8", "tq2_gemv_fused", "tq2_gemv_i8_fused",
             "tq2_gemv_gate_up_silu", "tq2_gemv_i8_requant", "tq2_gemm_workspace_bytes", "tq2_gemm",
-            "tq2_gemm_noalloc")
+            "tq2_gemm_i8q_workspace_bytes", "tq2_gemm_i8q", "tq2_gemm_noalloc")
 TQ2_ERR_SCRATCH = 7
 TQ2_GEMM_SCRATCH_BYTES = 4194304
 
@@ -381,6 +385,30 @@ def tq2_gemm(codes, scales, x, y=None, ws=None, stream=None):
     _placed(codes=codes, scales=scales, x=x, y=y, ws=ws)
     _check("tq2_gemm", _lib.tq2_gemm(_ptr(codes), _ptr(scales), N, K, _ptr(x), M, _ptr(y), _ptr(ws), _wsb(ws),
                                       _stream(stream)))
+    return y.view(M, N)
+
+
+def tq2_gemm_i8q_workspace_bytes(N, K, M):
+    return int(_lib.tq2_gemm_i8q_workspace_bytes(N, K, M))
+
+
+def tq2_gemm_i8q(codes, scales, x_q, s, y=None, ws=None, stream=None):
+    """Y[M][N]: the int8 matvec of every row of x_q (shape [M, K], int8,
+    quantized with s); allocates the workspace when none is given."""
+    N, K = _shape(codes, scales)
+    if not isinstance(x_q, torch.Tensor) or x_q.dim() != 2 or x_q.shape[1] != K:
+        raise ValueError(f"x_q must be a [M, {K}] tensor")
+    M = x_q.shape[0]
+    _dev(x_q, "x_q", (torch.int8,), M * K)
+    y = _out(y, "y", M * N, torch.float32, codes.device)
+    need = tq2_gemm_i8q_workspace_bytes(N, K, M)
+    if ws is None and need and need != 2 ** 64 - 1:
+        ws = torch.empty(need, dtype=torch.uint8, device=codes.device)
+    if ws is not None and need and need != 2 ** 64 - 1:
+        _dev(ws, "ws", None, need // ws.element_size(), at_least=True)
+    _placed(codes=codes, scales=scales, x_q=x_q, y=y, ws=ws)
+    _check("tq2_gemm_i8q", _lib.tq2_gemm_i8q(_ptr(codes), _ptr(scales), N, K, _ptr(x_q), M, float(s), _ptr(y),
+                                              _ptr(ws), _wsb(ws), _stream(stream)))
     return y.view(M, N)
 
 

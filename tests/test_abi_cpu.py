@@ -184,6 +184,32 @@ def test_error_paths_gemm(tq2):
 
 
 @no_gpu
+def test_error_paths_gemm_i8q(tq2):
+    lib = tq2.lib()
+    N, K, M = 256, 4096, 16  # K split in 4: int64 partials
+    need = lib.tq2_gemm_i8q_workspace_bytes(N, K, M)
+    assert need == 4 * M * N * 8
+    assert lib.tq2_gemm_i8q_workspace_bytes(N, K, 1) == 0       # the one-token kernel
+    assert lib.tq2_gemm_i8q_workspace_bytes(4096, 4096, 16) == 0  # 256 row sets: no split
+    bad = ctypes.c_size_t(-1).value
+    assert lib.tq2_gemm_i8q_workspace_bytes(N, 1000, M) == bad
+    assert lib.tq2_gemm_i8q_workspace_bytes(N, 65536, M) == bad  # above the int8 limit
+    assert lib.tq2_gemm_i8q_workspace_bytes(N, K, 0) == bad
+    c, s = A, A + 2 ** 24
+    xq, y, ws = A + 2 ** 26, A + 2 ** 27, A + 2 ** 28
+
+    def g(xx=xq, MM=M, yy=y, w=ws, wb=need, KK=K, sc=0.5):
+        return lib.tq2_gemm_i8q(P(c), P(s), N, KK, P(xx), MM, sc, P(yy), P(w), wb, None)
+
+    assert g(MM=0) == 1 and g(MM=65537) == 1 and g(KK=1000) == 2 and g(KK=65536) == 2
+    assert g(xx=xq + 2) == 3 and g(yy=y + 2) == 3
+    assert g(sc=0.0) == 5 and g(sc=float("nan")) == 5 and g(sc=float("inf")) == 5
+    assert g(w=0) == 4 and g(wb=need - 1) == 4 and g(w=ws + 16) == 4
+    assert g(yy=xq) == 1                     # y overlapping x_q
+    assert g(w=y) == 4                       # workspace overlapping y
+
+
+@no_gpu
 def test_gemm_workspace_only_for_split_k(tq2):
     """The 16384-row shapes run without a K split (no workspace), and so do
     4096 rows below K = 16384 (one row group per wave); 256 rows, and 4096

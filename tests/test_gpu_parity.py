@@ -610,6 +610,62 @@ def test_gemm_parity(tq2, N, K, M):
         _check_f16(Yc[m], ref[m], _tol(s, X[m], N, K), key=f"gemm {N}x{K} M={M}")
 
 
+# (N, K, M): the batched int8 matvec's plans (row groups per wave 4, 2, 1;
+# K split or not; one or two steps per load batch), ragged N and token tiles,
+# K up to the int8 limit, and M = 1 (the one-token kernel)
+GEMM_I8_SHAPES = [(16384, 4096, 16), (4096, 16384, 16), (4096, 4096, 8), (4608, 4096, 5), (256, 4096, 16),
+                  (33, 768, 3), (1000, 1280, 17), (3, 256, 40), (7, 65280, 3), (4096, 12288, 2),
+                  (300, 4352, 33), (16384, 4096, 1)]
+
+
+@pytest.mark.parametrize("N,K,M", GEMM_I8_SHAPES)
+def test_gemm_i8q_bit_exact(tq2, N, K, M):
+    """tq2_gemm_i8q against the oracle and against tq2_gemv_i8q on every
+    token, bit for bit, with a workspace exactly as large as asked for."""
+    _, c, s_, x = _packed(7000 + N + M, N, K)
+    g = synth.rng(7100 + M)
+    X = np.stack([synth.activations(g, K) for _ in range(M)])
+    s = np.float32(np.float32(np.abs(X.astype(np.float32)).max()) / np.float32(100))
+    XQ = np.stack([oracle.quantize_i8(synth.bits(X[m]), s) for m in range(M)])
+    dc, ds = _to_dev(c, s_)
+    XQd = torch.from_numpy(XQ).to(DEV)
+    need = tq2.tq2_gemm_i8q_workspace_bytes(N, K, M)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV) if need else None
+    Y = tq2.tq2_gemm_i8q(dc, ds, XQd, s, ws=ws)
+    Y2 = tq2.tq2_gemm_i8q(dc, ds, XQd, s, ws=ws)
+    ys = [tq2.tq2_gemv_i8q(dc, ds, XQd[m].contiguous(), s) for m in range(min(M, 4))]
+    torch.cuda.synchronize()
+    ref = oracle.gemm_i8q(c, s_, N, K, XQ, s)
+    Yc = Y.cpu().numpy()
+    assert np.array_equal(Yc.view(np.uint32), ref.view(np.uint32))
+    assert torch.equal(Y, Y2)
+    for m, y in enumerate(ys):
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), Yc[m].view(np.uint32))
+
+
+def test_gemm_i8q_tokens_independent_and_extreme_scales(tq2):
+    """A token's output does not depend on the other tokens (a permutation of
+    the tokens permutes the outputs, bit for bit); scales at the top and
+    bottom of binary16 and saturated activations stay exact."""
+    N, K, M = 4096, 4096, 16
+    _, c, s_, _ = _packed(7200, N, K)
+    s_ = s_.copy()
+    s_[0, 0], s_[1, 1], s_[17, 3], s_[4095, 15] = 0x7BFF, 0x0001, 0x7BFF, 0x0400
+    g = synth.rng(7201)
+    XQ = g.integers(-128, 128, size=(M, K), dtype=np.int8)
+    XQ[3, :] = 127
+    XQ[4, :] = -128
+    s = np.float32(0.02)
+    dc, ds = _to_dev(c, s_)
+    Y = tq2.tq2_gemm_i8q(dc, ds, torch.from_numpy(XQ).to(DEV), s)
+    perm = np.array([5, 2, 15, 0, 9, 3, 1, 4, 14, 6, 8, 13, 7, 10, 12, 11])
+    Yp = tq2.tq2_gemm_i8q(dc, ds, torch.from_numpy(np.ascontiguousarray(XQ[perm])).to(DEV), s)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_i8q(c, s_, N, K, XQ, s)
+    assert np.array_equal(Y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert torch.equal(Yp, Y[torch.from_numpy(perm).to(DEV)])
+
+
 def _gemm_sweep_cases(seed=7):
     """Seeded shapes for the batched planner, one per (N range, M range):
     N in 1..300, 1000..6000 or 8000..20000; M = 1, 2..4, 5..16 or 17..40;
