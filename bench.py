@@ -389,6 +389,8 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
     ("batched gate 16384x4096, 1 token per call (tq2_gemm)", 16384, 4096, "gemm1", 1005),
     ("batched q/o 4096x4096, 4 tokens per call (tq2_gemm)", 4096, 4096, "gemm4", 1006),
     ("batched q/o 4096x4096, 16 tokens per call (tq2_gemm)", 4096, 4096, "gemm16", 1007),
+    ("batched down 4096x16384 int8, 16 tokens per call (tq2_gemm_i8q)", 4096, 16384, "gemm_i8q16", 1008),
+    ("batched gate 16384x4096 int8, 16 tokens per call (tq2_gemm_i8q)", 16384, 4096, "gemm_i8q16", 1009),
     # the adjacent entry points, each a single call on its own shape
     ("next: fused q/k/v 4096+256+256 x 4096 fp16 (tq2_gemv_fused)", 4096, 4096, "qkv", 1006),
     ("next: fused q/k/v 4096+256+256 x 4096 int8 (tq2_gemv_i8_fused)", 4096, 4096, "qkv_i8", 1006),
@@ -409,6 +411,7 @@ WARM_SECONDS = 0.25
 REQUANT_S_OUT = 0.05
 CPU_TIMED_KINDS = ("f16", "f16_out", "gate_up", "i8", "i8q")
 GEMM_TOKENS = {"gemm16": 16, "gemm1": 1, "gemm4": 4}
+GEMM_I8_TOKENS = {"gemm_i8q16": 16}  # tq2_gemm_i8q: pre-quantized int8 tokens
 
 
 def config_bytes(kind, N, K, rows):
@@ -419,6 +422,8 @@ def config_bytes(kind, N, K, rows):
         return N * K * 66 // 256 + 2 * K + N  # int8 output
     if kind in GEMM_TOKENS:
         return N * K * 66 // 256 + GEMM_TOKENS[kind] * (2 * K + 4 * N)  # weights once, M x and M y
+    if kind in GEMM_I8_TOKENS:
+        return N * K * 66 // 256 + GEMM_I8_TOKENS[kind] * (K + 4 * N)  # weights once, M x_q and M y
     if kind == "i8q":
         return N * K * 66 // 256 + 4 * N + K  # x_q read once (1 byte per element)
     return sum(Ni * K * 66 // 256 + 4 * Ni for Ni in rows) + 2 * K  # x read once
@@ -455,6 +460,13 @@ class ConfigCase:
         self.X16 = None
         if kind in GEMM_TOKENS:
             self.X16 = torch.stack([synth.torch_activations(seed + 1 + m, K) for m in range(GEMM_TOKENS[kind])])
+        self.XQ = None
+        if kind in GEMM_I8_TOKENS:
+            # M tokens quantized with one static scale: fp32(max|X|) / 100 over all of them
+            self.X16 = torch.stack([synth.torch_activations(seed + 1 + m, K)
+                                    for m in range(GEMM_I8_TOKENS[kind])])
+            self.s = float(np.float32(np.abs(self.X16.cpu().numpy().astype(np.float32)).max()) / np.float32(100))
+            self.XQ = torch.stack([tq2.tq2_quantize_i8(self.X16[m], self.s) for m in range(self.X16.shape[0])])
         self.xq = tq2.tq2_quantize_i8(x, self.s) if kind == "i8q" else None
         self.nbytes = config_bytes(kind, N, K, self.rows)
         self.wbytes = sum(self.rows) * K * 66 // 256
@@ -462,6 +474,8 @@ class ConfigCase:
     def out_buffer(self, torch):
         if self.kind in GEMM_TOKENS:
             return torch.empty(GEMM_TOKENS[self.kind], self.N, dtype=torch.float32, device="cuda")
+        if self.kind in GEMM_I8_TOKENS:
+            return torch.empty(GEMM_I8_TOKENS[self.kind], self.N, dtype=torch.float32, device="cuda")
         if self.kind == "requant":
             return torch.empty(self.N, dtype=torch.int8, device="cuda")
         if self.kind == "silu":
@@ -476,6 +490,8 @@ class ConfigCase:
             return tq2.tq2_gemv_gate_up(mats[0][0], mats[0][1], mats[1][0], mats[1][1], x, y=y)
         if k in GEMM_TOKENS:
             return tq2.tq2_gemm(mats[0][0], mats[0][1], x, y=y, ws=ws)
+        if k in GEMM_I8_TOKENS:
+            return tq2.tq2_gemm_i8q(mats[0][0], mats[0][1], x, self.s, y=y, ws=ws)
         if k == "qkv":
             return tq2.tq2_gemv_fused(mats, x, y=y)
         if k == "qkv_i8":
@@ -493,6 +509,8 @@ class ConfigCase:
     def activation(self):
         if self.kind in GEMM_TOKENS:
             return self.X16
+        if self.kind in GEMM_I8_TOKENS:
+            return self.XQ
         if self.kind == "i8q":
             return self.xq
         return self.x
@@ -564,6 +582,15 @@ class ConfigCase:
             fns = []
             rec.update(rule="fp16 bounds of g and u propagated through silu(g)*u", max_err_over_bound=round(r, 6),
                        passed=r <= 1.0)
+        elif kind in GEMM_I8_TOKENS:
+            ch, sh = packed[0]
+            Xh = self.X16.cpu().numpy()
+            XQ_ref = np.stack([oracle.quantize_i8(synth.bits(Xh[m]), self.s) for m in range(Xh.shape[0])])
+            ok = np.array_equal(self.XQ.cpu().numpy(), XQ_ref)
+            ref = oracle.gemm_i8q(ch, sh, self.N, K, XQ_ref, self.s)
+            ok = ok and np.array_equal(yg.view(np.uint32), ref.view(np.uint32))
+            fns = []
+            rec.update(rule="bit-exact (x_q of every token and y)", passed=bool(ok))
         else:
             assert kind in GEMM_TOKENS
             ch, sh = packed[0]
@@ -641,6 +668,9 @@ def time_configs(torch, tq2, synth, probes, reps, max_calls, with_cpu):
         case = ConfigCase(torch, tq2, synth, label, N, K, kind, seed, want_host=with_cpu)
         rec = {"bytes_per_call": int(case.nbytes)}
         ws = None
+        if kind in GEMM_I8_TOKENS:
+            ws = torch.empty(max(256, tq2.tq2_gemm_i8q_workspace_bytes(N, K, GEMM_I8_TOKENS[kind])),
+                             dtype=torch.uint8, device="cuda")
         if kind in GEMM_TOKENS:
             ws = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(N, K, GEMM_TOKENS[kind])), dtype=torch.uint8,
                              device="cuda")
@@ -676,8 +706,8 @@ def time_configs(torch, tq2, synth, probes, reps, max_calls, with_cpu):
                     "pct_of_read_probe": round(100 * us_rd / us, 1),
                     "rotation_copies": ncopy, "calls_per_graph": ncall,
                     "bytes_rotated": int(ncall * case.nbytes), "trace_marker": MARK_CONFIG + ci})
-        if kind in GEMM_TOKENS:
-            rec["tokens_per_s"] = round(GEMM_TOKENS[kind] * 1e6 / us, 1)
+        if kind in GEMM_TOKENS or kind in GEMM_I8_TOKENS:
+            rec["tokens_per_s"] = round({**GEMM_TOKENS, **GEMM_I8_TOKENS}[kind] * 1e6 / us, 1)
         if "cpu_oracle" in rec:
             rec["gpu_speedup_vs_cpu_nproc"] = round(rec["cpu_oracle"]["us_per_call_nproc"] / us, 1)
         out[label] = rec
@@ -1223,6 +1253,14 @@ def main():
                     one = out["roofline"]["us_per_launch"]
                 if one is not None:
                     rec[f"speedup_vs_{m}_gemv"] = round(m * one / rec["us_per_call"], 2)
+            if CONFIGS[ci][3] in GEMM_I8_TOKENS:
+                # against that many tq2_gemv_i8q calls of the same shape, where timed
+                m = GEMM_I8_TOKENS[CONFIGS[ci][3]]
+                N_, K_ = CONFIGS[ci][1], CONFIGS[ci][2]
+                one = next((out["configs"][c[0]]["us_per_call"] for c in CONFIGS
+                            if c[3] == "i8q" and (c[1], c[2]) == (N_, K_) and c[0] in out["configs"]), None)
+                if one is not None:
+                    rec[f"speedup_vs_{m}_gemv_i8q"] = round(m * one / rec["us_per_call"], 2)
         c0, c1 = (out["configs"][CONFIGS[i][0]]["us_per_call"] for i in (0, 1))
         qkv = next(out["configs"][c[0]] for c in CONFIGS if c[3] == "qkv")
         qkv["three_single_calls_us"] = round(c1 + 2 * c0, 3)

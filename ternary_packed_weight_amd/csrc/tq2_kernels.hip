@@ -2007,12 +2007,23 @@ __device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint3
   o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
+constexpr int kStepTileI8 = kTok * kBlock;  // x_q of one step for one tile: 4 KiB
+
 // Workgroup: C waves, the C chunks of steps of one K-split of one row set
 // (U row groups of 16) for one tile of 16 tokens; their int64 sums meet in
 // LDS.  Grid: (row sets, K-splits, token tiles).
-template <int U, int T, int C>
+//
+// x_q reaches the lanes one of two ways.  XL: straight to LDS, each load
+// instruction bringing four tokens' 256 contiguous bytes of a step, token t's
+// 16-byte chunk c stored at position c ^ t of its 256 bytes, so that the 16
+// tokens of a later ds_read_b128 fall in distinct banks; then read back in
+// operand order.  Otherwise each lane loads its own token's 64 bytes.
+template <int U, int T, int C, bool XL>
 __global__ __launch_bounds__(64 * C) void k_gemm_i8(GemmI8Args a) {
-  __shared__ int64_t red[C][U][4][64];
+  constexpr int kXBytes = XL ? C * T * kStepTileI8 : 0;
+  constexpr int kRedBytes = C * U * 4 * 64 * 8;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kXBytes > kRedBytes ? kXBytes : kRedBytes];
+  int64_t(*red)[U][4][64] = reinterpret_cast<int64_t(*)[U][4][64]>(smem);
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4, i = lane & 15;
   const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2054,13 +2065,27 @@ __global__ __launch_bounds__(64 * C) void k_gemm_i8(GemmI8Args a) {
     // issue, in this order (loads complete in issue order): this lane's 64
     // x_q bytes of each step (L2), the code words (HBM), the scales
     uint4 xv[T][4];
+    uint8_t* xs = smem + c * (T * kStepTileI8);  // XL: this wave's x_q
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int s = s0 + t < s_end ? s0 + t : s0;  // in range
-      const int xoff = (int)(i * a.K + 256 * (int64_t)s + 64 * G);
+      if constexpr (XL) {
+        // load n: tokens 4n + (lane >> 4); lane l stores chunk (l & 15) ^ token
+        // of its token at position l & 15
 #pragma unroll
-      for (int n = 0; n < 4; ++n) xv[t][n] = load_b128(xr, xoff + 16 * n);
+        for (int n = 0; n < 4; ++n) {
+          const int tk = 4 * n + (lane >> 4);
+          const int ch = (lane & 15) ^ tk;
+          const int off = (int)(tk * a.K + 256 * (int64_t)s + 16 * ch);
+          load_b128_lds(xr, off, xs + t * kStepTileI8 + 1024 * n);
+        }
+      } else {
+        const int xoff = (int)(i * a.K + 256 * (int64_t)s + 64 * G);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) xv[t][n] = load_b128(xr, xoff + 16 * n);
+      }
     }
+    if constexpr (XL) __builtin_amdgcn_sched_barrier(0);  // keeps the order the wait counts on
     uint4 w[T][U];
     uint16_t d[T][U][4];
 #pragma unroll
@@ -2089,6 +2114,14 @@ __global__ __launch_bounds__(64 * C) void k_gemm_i8(GemmI8Args a) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (s0 + t >= s_end) break;  // uniform
+      if constexpr (XL) {
+        // this step's x_q is in LDS once the loads issued after it are all
+        // that is left in flight (its later steps, the codes, the scales)
+        wait_vm_at((T - 1 - t) * 4 + 5 * T * U);
+        const uint8_t* xl = xs + t * kStepTileI8 + 256 * i;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xv[t][k] = *reinterpret_cast<const uint4*>(xl + 16 * ((4 * G + k) ^ i));
+      }
       const uint32_t xw[16] = {xv[t][0].x, xv[t][0].y, xv[t][0].z, xv[t][0].w,
                                xv[t][1].x, xv[t][1].y, xv[t][1].z, xv[t][1].w,
                                xv[t][2].x, xv[t][2].y, xv[t][2].z, xv[t][2].w,
@@ -2126,6 +2159,7 @@ __global__ __launch_bounds__(64 * C) void k_gemm_i8(GemmI8Args a) {
 
   // chunk sums meet in LDS (int64: exact in any order); wave 0 stores
   if (C > 1) {
+    if constexpr (XL) __syncthreads();  // all x_q reads done before the sums overwrite it
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -2172,24 +2206,38 @@ __global__ __launch_bounds__(256) void k_gemm_i8_reduce(const int64_t* __restric
 GemmPlan plan_gemm_i8(int64_t N, int64_t K, int64_t M) {
   GemmPlan p;
   p.TT = 1;
-  p.xl = false;
+  // x_q through LDS from 8 tokens (16384x4096 at 16 tokens 14.2 -> 13.7 us,
+  // 4096x16384 15.6 -> 12.1; at 2 and 4 tokens the per-lane loads are
+  // 0.05-0.3 us faster, at 8 they tie)
+  p.xl = M >= 8;
   p.mt = (M + kTok - 1) / kTok;
   p.zt = p.mt;
   const int64_t steps = K / kBlock;
   const int64_t groups = (N + kTileRows16 - 1) / kTileRows16;
-  // row groups per wave: the most of 4, 2, 1 that still leaves more row
-  // sets than half the CUs (building a step's B operands costs ~50
-  // instructions, a row group's decode ~30, so fewer rows per wave cost
-  // little and spare the split)
+  // row groups per wave: the most of 4, 2, 1 that still gives two
+  // workgroups per CU, then 4-wave workgroups; otherwise 1 row group and
+  // 8-wave workgroups.  (Building a step's B operands costs ~50
+  // instructions and a row group's decode ~30 per step, so fewer rows per
+  // wave cost little; what counts is that each wave's work comes in more
+  // than one load batch, so that its compute overlaps its later loads.)
+  // Measured on MI355X, same box, against 4 row groups in 8-wave
+  // workgroups: 16384x4096 at 8/16/32 tokens 13.4/13.7/20.9 ->
+  // 9.7/10.4/15.7 us, 4608x4096 at 8 8.2 -> 7.1; 4096x16384 at 16 (1 row
+  // group, 8 waves) 12.1 either way; 8-wave against 4-wave workgroups for
+  // 4096x4096 at 4/8 tokens 5.57/5.78 against 5.90/5.92.
   int64_t rsets = groups;
+  bool two = false;
   for (int u = 4; u >= 1; u /= 2) {
     p.U = u;
     rsets = (groups + u - 1) / u;
-    if (2 * rsets * p.zt > device_cus()) break;
+    if (rsets * p.zt >= 2 * device_cus()) {
+      two = true;
+      break;
+    }
   }
   const bool wide = rsets * p.zt >= device_cus() || steps >= 32;
   p.T = wide ? 2 : 1;
-  p.S = (wide && steps >= 16) ? 8 : 4;
+  p.S = (!two && wide && steps >= 16) ? 8 : 4;
   const int64_t per_split = (int64_t)p.S * p.T;
   int64_t max_splits = steps / per_split;
   if (max_splits < 1) max_splits = 1;
@@ -2209,14 +2257,19 @@ size_t gemm_i8_workspace_bytes(int64_t N, int64_t K, int64_t M) {
   return (size_t)plan_gemm_i8(N, K, M).part_bytes;
 }
 
-template <int U>
+template <int U, bool XL>
 static void launch_gemm_i8_tile(const GemmPlan& p, dim3 grid, hipStream_t st, const GemmI8Args& a) {
   if (p.T == 2 && p.S == 8)
-    hipLaunchKernelGGL((k_gemm_i8<U, 2, 8>), grid, dim3(64 * 8), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_i8<U, 2, 8, XL>), grid, dim3(64 * 8), 0, st, a);
   else if (p.T == 2)
-    hipLaunchKernelGGL((k_gemm_i8<U, 2, 4>), grid, dim3(64 * 4), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_i8<U, 2, 4, XL>), grid, dim3(64 * 4), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_i8<U, 1, 4>), grid, dim3(64 * 4), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_i8<U, 1, 4, XL>), grid, dim3(64 * 4), 0, st, a);
+}
+template <int U>
+static void launch_gemm_i8_tile(const GemmPlan& p, dim3 grid, hipStream_t st, const GemmI8Args& a) {
+  if (p.xl) launch_gemm_i8_tile<U, true>(p, grid, st, a);
+  else launch_gemm_i8_tile<U, false>(p, grid, st, a);
 }
 
 hipError_t launch_gemm_i8(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,

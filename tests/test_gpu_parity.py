@@ -611,11 +611,12 @@ def test_gemm_parity(tq2, N, K, M):
 
 
 # (N, K, M): the batched int8 matvec's plans (row groups per wave 4, 2, 1;
-# K split or not; one or two steps per load batch), ragged N and token tiles,
-# K up to the int8 limit, and M = 1 (the one-token kernel)
+# 4- and 8-wave workgroups; K split or not; one or two steps per load batch;
+# x_q through LDS or per lane), ragged N and token tiles, K up to the int8
+# limit, and M = 1 (the one-token kernel)
 GEMM_I8_SHAPES = [(16384, 4096, 16), (4096, 16384, 16), (4096, 4096, 8), (4608, 4096, 5), (256, 4096, 16),
                   (33, 768, 3), (1000, 1280, 17), (3, 256, 40), (7, 65280, 3), (4096, 12288, 2),
-                  (300, 4352, 33), (16384, 4096, 1)]
+                  (300, 4352, 33), (16384, 4096, 1), (16384, 4096, 32)]
 
 
 @pytest.mark.parametrize("N,K,M", GEMM_I8_SHAPES)
