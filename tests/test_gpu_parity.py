@@ -801,8 +801,9 @@ def test_graph_capture_replay(tq2):
     the same calls run eagerly between the replays: every replay equals the
     eager result on the same inputs bit for bit (all kernels are
     deterministic).  Covers the split-K batched path (workspace plus the
-    reduce kernel), the two-tile batched path and the few-token one-pass
-    matvec (2 tokens at 4096x16384, whose LDS needs the raised limit)."""
+    reduce kernel), the two-tile batched path, the few-token one-pass
+    matvec (2 tokens at 4096x16384, whose LDS needs the raised limit) and
+    the batched int8 matvec (split K into int64 partials; x_q through LDS)."""
     (_, ca, sa, _), (_, cb, sb, _), (_, cc, scc, _) = (
         _packed(2300, 256, 4096), _packed(2301, 4096, 16384), _packed(2302, 1000, 1280))
     (dca, dsa), (dcb, dsb), (dcc, dsc) = _to_dev(ca, sa), _to_dev(cb, sb), _to_dev(cc, scc)
@@ -814,6 +815,11 @@ def test_graph_capture_replay(tq2):
     yi8, Yb, Yc = torch.empty(4096, device=DEV), torch.empty((20, 4096), device=DEV), torch.empty(
         (5, 1000), device=DEV)
     Y2 = torch.empty((2, 4096), device=DEV)
+    XQa, XQb = (torch.empty((16, 4096), dtype=torch.int8, device=DEV),
+                torch.empty((8, 16384), dtype=torch.int8, device=DEV))
+    YQa, YQb = torch.empty((16, 256), device=DEV), torch.empty((8, 4096), device=DEV)
+    wsq = torch.empty(max(256, tq2.tq2_gemm_i8q_workspace_bytes(256, 4096, 16)), dtype=torch.uint8, device=DEV)
+    assert tq2.tq2_gemm_i8q_workspace_bytes(256, 4096, 16) > 0  # int64 split sums and their reduce
     assert tq2.tq2_gemm_workspace_bytes(4096, 16384, 2) == 0  # the one-pass few-token route
     wsb = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(4096, 16384, 20)), dtype=torch.uint8, device=DEV)
     wsc = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(1000, 1280, 5)), dtype=torch.uint8, device=DEV)
@@ -828,14 +834,18 @@ def test_graph_capture_replay(tq2):
         tq2.tq2_gemm(dcb, dsb, Xb, y=Yb, ws=wsb)
         tq2.tq2_gemm(dcc, dsc, Xc, y=Yc, ws=wsc)
         tq2.tq2_gemm(dcb, dsb, X2, y=Y2)
+        tq2.tq2_gemm_i8q(dca, dsa, XQa, s_in, y=YQa, ws=wsq)
+        tq2.tq2_gemm_i8q(dcb, dsb, XQb, s_in, y=YQb)
 
-    outs = [ya, ygu, hh, yi8, Yb, Yc, Y2]
+    outs = [ya, ygu, hh, yi8, Yb, Yc, Y2, YQa, YQb]
 
     def fill(seed):
         g = synth.rng(seed)
         for t in (xa, xb, Xb, Xc, X2):
             vals = np.stack([synth.activations(g, t.shape[-1]) for _ in range(t.numel() // t.shape[-1])])
             t.copy_(torch.from_numpy(vals.reshape(t.shape)))
+        for t in (XQa, XQb):
+            t.copy_(torch.from_numpy(g.integers(-128, 128, size=tuple(t.shape), dtype=np.int8)))
 
     fill(2310)
     run()
@@ -851,7 +861,8 @@ def test_graph_capture_replay(tq2):
         got = [o.clone() for o in outs]
         run()
         torch.cuda.synchronize()
-        for name, a, b in zip(["gemv", "gate_up", "silu", "i8", "gemm_splitk_2tile", "gemm", "gemm_few"], got, outs):
+        for name, a, b in zip(["gemv", "gate_up", "silu", "i8", "gemm_splitk_2tile", "gemm", "gemm_few",
+                               "gemm_i8q_splitk", "gemm_i8q"], got, outs):
             assert torch.equal(a, b), (rep, name)
 
 
