@@ -466,7 +466,7 @@ class ConfigCase:
             self.X16 = torch.stack([synth.torch_activations(seed + 1 + m, K)
                                     for m in range(GEMM_I8_TOKENS[kind])])
             self.s = float(np.float32(np.abs(self.X16.cpu().numpy().astype(np.float32)).max()) / np.float32(100))
-            self.XQ = torch.stack([tq2.tq2_quantize_i8(self.X16[m], self.s) for m in range(self.X16.shape[0])])
+            self.XQ = tq2.tq2_quantize_i8(self.X16, self.s)  # all tokens in one call: [M][K]
         self.xq = tq2.tq2_quantize_i8(x, self.s) if kind == "i8q" else None
         self.nbytes = config_bytes(kind, N, K, self.rows)
         self.wbytes = sum(self.rows) * K * 66 // 256

@@ -133,7 +133,10 @@ int32_t tq2_gemv_gate_up(const uint8_t *codes_g, const uint16_t *scales_g,
  * wNa8o8 requires int8 activations": clamp(round(x/s), -128, 127)).
  * Precisely: v = x/s as one IEEE fp32 division, rint (ties to even),
  * clamped to [-128,127] before conversion.  s must be finite and > 0;
- * non-finite x gives an unspecified x_q.  x_q[K] is int8 in natural order. */
+ * non-finite x gives an unspecified x_q.  x_q[K] is int8 in natural order.
+ * Elementwise, so K is any positive multiple of 256 up to
+ * TQ2_MAX_TOKENS * TQ2_MAX_K: the M tokens of a tq2_gemm_i8q call
+ * (x [M][K] row-major) are quantized in one call (TQ2_ERR_SHAPE otherwise). */
 int32_t tq2_quantize_i8(const uint16_t *x, int64_t K, float s, int8_t *x_q,
                         tq2_stream_t stream);
 

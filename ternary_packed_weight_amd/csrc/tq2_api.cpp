@@ -200,7 +200,8 @@ int32_t tq2_gemv_gate_up_silu(const uint8_t* codes_g, const uint16_t* scales_g,
 }
 
 int32_t tq2_quantize_i8(const uint16_t* x, int64_t K, float s, int8_t* x_q, tq2_stream_t stream) {
-  TQ2_TRY(check_shape(1, K, TQ2_MAX_K));
+  // elementwise: any whole number of 256-blocks up to a full batch of tokens
+  if (K < TQ2_BLOCK || K % TQ2_BLOCK != 0 || K > (int64_t)TQ2_MAX_TOKENS * TQ2_MAX_K) return TQ2_ERR_SHAPE;
   if (!x || !x_q) return TQ2_ERR_ARG;
   if (!aligned(x, 16) || !aligned(x_q, 16)) return TQ2_ERR_ALIGN;
   TQ2_TRY(check_scale(s));

@@ -266,7 +266,7 @@ def tq2_quantize_i8(x, s, x_q=None, stream=None):
     x_q = _out(x_q, "x_q", K, torch.int8, x.device)
     _placed(x=x, x_q=x_q)
     _check("tq2_quantize_i8", _lib.tq2_quantize_i8(_ptr(x), K, float(s), _ptr(x_q), _stream(stream)))
-    return x_q
+    return x_q.view(x.shape)
 
 
 def _workspace(op, N, K, ws, device):

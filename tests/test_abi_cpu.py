@@ -115,6 +115,7 @@ def test_error_paths_int8(tq2):
     assert q == 1                              # partials alias y
     assert lib.tq2_quantize_i8(P(A), 256, ctypes.c_float(0.0), P(A + 4096), None) == 5
     assert lib.tq2_quantize_i8(P(A), 255, ctypes.c_float(1.0), P(A + 4096), None) == 2
+    assert lib.tq2_quantize_i8(P(A), (65536 * 65536) + 256, ctypes.c_float(1.0), P(A + 4096), None) == 2
     assert lib.tq2_quantize_i8(P(A), 256, ctypes.c_float(1.0), P(A + 96), None) == 1
     assert lib.tq2_quantize_i8(P(A), 256, ctypes.c_float(1.0), P(A + 4097), None) == 3
 

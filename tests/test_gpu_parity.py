@@ -630,6 +630,9 @@ def test_gemm_i8q_bit_exact(tq2, N, K, M):
     XQ = np.stack([oracle.quantize_i8(synth.bits(X[m]), s) for m in range(M)])
     dc, ds = _to_dev(c, s_)
     XQd = torch.from_numpy(XQ).to(DEV)
+    # all M tokens quantized in one call, bit-equal to the oracle per token
+    XQg = tq2.tq2_quantize_i8(torch.from_numpy(np.ascontiguousarray(X, np.float16)).to(DEV), s)
+    assert XQg.shape == (M, K) and np.array_equal(XQg.cpu().numpy(), XQ)
     need = tq2.tq2_gemm_i8q_workspace_bytes(N, K, M)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV) if need else None
     Y = tq2.tq2_gemm_i8q(dc, ds, XQd, s, ws=ws)
