@@ -265,8 +265,11 @@ size_t tq2_gemm_i8q_workspace_bytes(int64_t N, int64_t K, int64_t M);
  * least that many bytes, 256-byte aligned, not overlapping x_q or Y
  * (TQ2_ERR_WORKSPACE otherwise); its contents on entry do not matter.
  * Otherwise ws may be NULL.  One kernel on `stream` (two when K is split);
- * M = 1 runs tq2_gemv_i8q's kernel.  The weights are streamed once for all
- * M tokens. */
+ * M = 1 runs tq2_gemv_i8q's kernel; M = 2 to 4 with K of 1, 2 or 4 chunks
+ * of 4096 a one-pass VALU matvec while the x_q it stages over all its
+ * workgroups (workgroups x M x K bytes) stays within 24 MiB (no workspace);
+ * other calls the matrix cores.  The weights are streamed once for all M
+ * tokens. */
 int32_t tq2_gemm_i8q(const uint8_t *codes, const uint16_t *scales, int64_t N,
                      int64_t K, const int8_t *x_q, int64_t M, float s, float *y,
                      void *ws, size_t ws_bytes, tq2_stream_t stream);

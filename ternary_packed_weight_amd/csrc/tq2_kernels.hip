@@ -1889,6 +1889,218 @@ __global__ __launch_bounds__(MAXT) void k_gemv_i8(MatSet ms, int64_t K,
   }
 }
 
+// The int8 matvec for M = 2..4 tokens of pre-quantized activations (the
+// small-M batched int8 matvec): k_gemv_i8's waves, rows, loads and order,
+// with the M tokens' x_q staged side by side in LDS.  Each code word is
+// masked once and then dotted with every token's x_q (the same v_dot4 sums
+// as lane_dot_i8), so the weights are streamed and decoded once for all M
+// tokens.  The sums are exact integers: every token's output equals
+// tq2_gemv_i8q's bit for bit.  Output y[M][N].
+template <int M>
+__host__ __device__ inline size_t i8m_lds_bytes(int C, int S, int R) {
+  return (size_t)M * ((size_t)C * 4 * 64 * 16 + (size_t)C * 64 * 16) + 16 + (size_t)M * C * S * R * 8;
+}
+
+template <int R, int M, int CT, int MAXT>
+__global__ __launch_bounds__(MAXT) void k_gemv_i8m(MatSet ms, int64_t K, const int8_t* __restrict__ xq_in,
+                                                   float s, float* __restrict__ y, Split sp) {
+  extern __shared__ uint4 lds[];
+  const int C = CT ? CT : sp.C, S = sp.S;
+  uint4* xs = lds;                                                  // [M][C][4][64]
+  int* gsum = reinterpret_cast<int*>(lds + M * C * 4 * 64);         // [M][C][64][4]
+  uint4* sink = lds + M * C * 4 * 64 + M * C * 64;                  // [1]
+  int64_t* red = reinterpret_cast<int64_t*>(sink + 1);              // [M][C*S][R]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = __builtin_amdgcn_readfirstlane(wave / C);
+  const int c = wave - slot * C;
+  const int row0 = ((int)blockIdx.x * S + slot) * R;
+  const int64_t k0 = (int64_t)c * kChunk + (int64_t)lane * kLaneK;
+  const bool active = k0 < K;
+  const int64_t kk = active ? k0 : 0;
+  const int64_t row_bytes = K / 4;
+  const int64_t BK = K / kBlock;
+  const int64_t N = ms.rows;
+  const int ngroups = (int)(K / 16);
+
+  // (1) loads: every token's x_q (16 bytes per group of 16, clamped), the
+  //     workgroup barrier, then the first rows
+  constexpr int XP = f16m_stage_passes(CT, MAXT);
+  uint4 xa[M][XP];
+#pragma unroll
+  for (int t = 0; t < M; ++t) {
+    const __amdgpu_buffer_rsrc_t xr = rsrc(xq_in + t * K, (uint32_t)K);
+#pragma unroll
+    for (int p = 0; p < XP; ++p) xa[t][p] = load_b128(xr, 16 * (tid + p * (int)blockDim.x));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();  // x_q of every wave ahead of any weight request (see k_gemv_f16)
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 w[R];
+  uint16_t hs[R];
+  load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs, 0, kRowWindow<R>);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (2) stage every token as k_gemv_i8 stages its one
+#pragma unroll
+  for (int t = 0; t < M; ++t) {
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+      const int m = tid + p * (int)blockDim.x;
+      const bool staged = m < ngroups;
+      const uint32_t bw[4] = {xa[t][p].x, xa[t][p].y, xa[t][p].z, xa[t][p].w};
+      uint32_t mb[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mb[i] = bw[i >> 2] >> (8 * (i & 3));
+      uint32_t dw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = __builtin_amdgcn_perm(mb[4 + j], mb[j], 0x0C0C0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(mb[12 + j], mb[8 + j], 0x04000C0Cu);
+        dw[j] = lo | hi;
+      }
+      const int ch = m >> 8, ln = (m >> 2) & 63, gg = m & 3;
+      *(staged ? xs + ((t * C + ch) * 4 + gg) * 64 + ln : sink) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+      int gs = dot4(dw[0], 0x01010101u, 0);
+      gs = dot4(dw[1], 0x01010101u, gs);
+      gs = dot4(dw[2], 0x01010101u, gs);
+      gs = dot4(dw[3], 0x01010101u, gs);
+      *(staged ? gsum + ((t * C + ch) * 64 + ln) * 4 + gg : reinterpret_cast<int*>(sink)) = gs;
+    }
+  }
+  __syncthreads();
+
+  // (3) this lane's x_q and seed per token, then the rest of the rows
+  uint32_t xq[M][16];
+  int seed[M];
+#pragma unroll
+  for (int t = 0; t < M; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 tt = xs[((t * C + c) * 4 + i) * 64 + lane];
+      xq[t][4 * i + 0] = tt.x; xq[t][4 * i + 1] = tt.y; xq[t][4 * i + 2] = tt.z; xq[t][4 * i + 3] = tt.w;
+    }
+    const int4 gs4 = reinterpret_cast<const int4*>(gsum)[(t * C + c) * 64 + lane];
+    seed[t] = -((gs4.x + gs4.y) + (gs4.z + gs4.w));
+  }
+  if constexpr (kRowWindow<R> < R) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_rows<R>(ms, row0, kk, row_bytes, BK, w, hs, kRowWindow<R>, R);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  int64_t acc[M][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t keep = (row0 + r < ms.rows ? 0xFFFFu : 0u) & (0u - (uint32_t)active);
+    const uint16_t h = (uint16_t)(hs[r] & keep);
+    // the fields of bit pairs 0..3 in bytes, once for all tokens (as lane_dot_i8)
+    const uint32_t ws[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+    uint32_t mk[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      mk[g][0] = ws[g] & 0x03030303u;
+      mk[g][1] = ws[g] & 0x0C0C0C0Cu;
+      mk[g][2] = ws[g] & 0x30303030u;
+      mk[g][3] = (ws[g] >> 6) & 0x03030303u;
+    }
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+      int a = seed[t], b = 0, cc = 0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        a = dot4(xq[t][4 * g + 0], mk[g][0], a);
+        b = dot4(xq[t][4 * g + 1], mk[g][1], b);
+        cc = dot4(xq[t][4 * g + 2], mk[g][2], cc);
+        a = dot4(xq[t][4 * g + 3], mk[g][3], a);
+      }
+      acc[t][r] = scaled_partial(h, a + (b >> 2) + (cc >> 4));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one row's masked words live at a time
+  }
+  const int rho = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < M; ++t) {
+    int64_t out[kOut<R>];
+    reduce_rows_i64<R>(acc[t], out);
+    if (C == 1) {
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < kOut<R>; ++i) {
+          const int rr = reduced_row<R>(i, rho);
+          if (rr >= 0 && row0 + rr < ms.rows) y[t * N + row0 + rr] = i8_epilogue(out[i], s);
+        }
+      }
+    } else if ((lane & 15) == 0) {
+#pragma unroll
+      for (int i = 0; i < kOut<R>; ++i) {
+        const int rr = reduced_row<R>(i, rho);
+        if (rr >= 0) red[(t * C * S + wave) * R + rr] = out[i];
+      }
+    }
+  }
+  if (C == 1) return;
+  __syncthreads();
+  if (c == 0 && lane < R) {
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+      int64_t tsum = red[(t * C * S + wave) * R + lane];
+      for (int cc = 1; cc < C; ++cc) tsum += red[(t * C * S + wave + cc) * R + lane];
+      if (row0 + lane < ms.rows) y[t * N + row0 + lane] = i8_epilogue(tsum, s);
+    }
+  }
+}
+
+// Launch of k_gemv_i8m: 4 row groups per workgroup for K of 1 and 2 chunks,
+// 2 for 4 chunks (512 threads), as k_gemv_f16m.
+static Split i8m_split(int64_t K) {
+  Split sp = pick_split(K, false);
+  sp.S = sp.C == 4 ? 2 : 4;
+  return sp;
+}
+static int i8m_rows_per_wave(int64_t rows, int64_t K, int64_t M) {
+  return pick_rows_per_wave(rows, (int)chunks_of(K), 16, M == 2 ? 4 : 2);
+}
+// x_q bytes k_gemv_i8m stages over all its workgroups (each stages every token)
+static int64_t i8m_staging_bytes(int64_t rows, int64_t K, int64_t M) {
+  const int R = i8m_rows_per_wave(rows, K, M);
+  const Split sp = i8m_split(K);
+  const int64_t nwg = ((rows + R - 1) / R + sp.S - 1) / sp.S;
+  return nwg * M * K;
+}
+
+template <int R, int M>
+static hipError_t run_gemv_i8m(const MatSet& m, int64_t K, const int8_t* xq, float s, float* y, hipStream_t st) {
+  const Split sp = i8m_split(K);
+  if (sp.C != 1 && sp.C != 2 && sp.C != 4) return hipErrorInvalidConfiguration;
+  const int64_t groups = (m.rows + R - 1) / R;
+  const dim3 grid((unsigned)((groups + sp.S - 1) / sp.S));
+  const size_t lds = i8m_lds_bytes<M>(sp.C, sp.S, R);
+  const dim3 block(64 * sp.C * sp.S);
+  // MAXT 512: the block is 512 threads for C = 2 and 4, 256 for C = 1
+  if ((int64_t)f16m_stage_passes(sp.C, 512) * block.x < K / 16 || block.x > 512 || lds > 160 * 1024)
+    return hipErrorInvalidConfiguration;
+  auto go = [&](auto kfn) -> hipError_t {
+    if (lds > 64 * 1024) {
+      const hipError_t e = set_lds_cap(reinterpret_cast<const void*>(kfn));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kfn, grid, block, lds, st, m, K, xq, s, y, sp);
+    return hipGetLastError();
+  };
+  if (sp.C == 1) return go(k_gemv_i8m<R, M, 1, 512>);
+  if (sp.C == 2) return go(k_gemv_i8m<R, M, 2, 512>);
+  return go(k_gemv_i8m<R, M, 4, 512>);
+}
+
+template <int M>
+static hipError_t launch_gemv_i8m(const MatSet& m, int64_t K, const int8_t* xq, float s, float* y, hipStream_t st) {
+  if constexpr (M == 2)
+    if (i8m_rows_per_wave(m.rows, K, M) == 4) return run_gemv_i8m<4, M>(m, K, xq, s, y, st);
+  return run_gemv_i8m<2, M>(m, K, xq, s, y, st);
+}
+
 template <int R, bool QUANT, bool PARTIALS, bool REQUANT>
 static hipError_t run_gemv_i8(const MatSet& m, int64_t K, const uint16_t* x, const int8_t* xq,
                               float s, float* y, int32_t* partials, const Requant& rq,
@@ -2252,8 +2464,22 @@ GemmPlan plan_gemm_i8(int64_t N, int64_t K, int64_t M) {
   return p;
 }
 
+// 2 to 4 tokens with K of 1, 2 or 4 chunks take the one-pass int8 matvec
+// (k_gemv_i8m) while its x_q staging stays within 24 MiB.  Measured on
+// MI355X against the matrix cores (us): 4096x4096 at 2/3/4 tokens
+// 5.44/5.52/5.56 -> 3.55/3.95/4.44, 256x4096 at 2 5.56 -> 2.82, 16384x4096
+// at 2 and 3 (8 and 24 MiB) 9.05/9.09 -> 6.33/8.57, 4096x16384 at 2 10.46 ->
+// 6.70; past the cap it loses: 16384x4096 at 4 (32 MiB) 10.1 against 9.2,
+// 4096x16384 at 3 (48 MiB) 11.2 against 10.6.
+constexpr int64_t kValuStagingBytesI8 = (int64_t)24 << 20;
+static bool gemm_i8_on_valu(int64_t N, int64_t K, int64_t M) {
+  const int64_t c = chunks_of(K);
+  return M >= 2 && M <= kValuTokens && (c == 1 || c == 2 || c == 4) &&
+         i8m_staging_bytes(N, K, M) <= kValuStagingBytesI8;
+}
+
 size_t gemm_i8_workspace_bytes(int64_t N, int64_t K, int64_t M) {
-  if (M == 1) return 0;  // the one-token int8 kernel (see launch_gemm_i8)
+  if (M == 1 || gemm_i8_on_valu(N, K, M)) return 0;  // the matvec kernels (see launch_gemm_i8)
   return (size_t)plan_gemm_i8(N, K, M).part_bytes;
 }
 
@@ -2282,6 +2508,16 @@ hipError_t launch_gemm_i8(const uint8_t* codes, const uint16_t* scales, int64_t 
     m.nmat = 1;
     m.rows = (int32_t)N;
     return launch_gemv_i8(m, K, nullptr, xq, s, y, nullptr, st);
+  }
+  if (gemm_i8_on_valu(N, K, M)) {
+    MatSet m{};
+    m.codes[0] = codes;
+    m.scales[0] = scales;
+    m.nmat = 1;
+    m.rows = (int32_t)N;
+    if (M == 2) return launch_gemv_i8m<2>(m, K, xq, s, y, st);
+    if (M == 3) return launch_gemv_i8m<3>(m, K, xq, s, y, st);
+    return launch_gemv_i8m<4>(m, K, xq, s, y, st);
   }
   const GemmPlan p = plan_gemm_i8(N, K, M);
   GemmI8Args a;

@@ -192,6 +192,10 @@ def test_error_paths_gemm_i8q(tq2):
     assert need == 4 * M * N * 8
     assert lib.tq2_gemm_i8q_workspace_bytes(N, K, 1) == 0       # the one-token kernel
     assert lib.tq2_gemm_i8q_workspace_bytes(4096, 4096, 16) == 0  # 256 row sets: no split
+    for m in (2, 3, 4):  # the one-pass few-token int8 matvec
+        assert lib.tq2_gemm_i8q_workspace_bytes(256, 4096, m) == 0
+        assert lib.tq2_gemm_i8q_workspace_bytes(256, 16384, m) == 0
+    assert lib.tq2_gemm_i8q_workspace_bytes(256, 12288, 2) > 0  # 3 chunks: matrix cores, K split
     bad = ctypes.c_size_t(-1).value
     assert lib.tq2_gemm_i8q_workspace_bytes(N, 1000, M) == bad
     assert lib.tq2_gemm_i8q_workspace_bytes(N, 65536, M) == bad  # above the int8 limit

@@ -616,7 +616,12 @@ def test_gemm_parity(tq2, N, K, M):
 # limit, and M = 1 (the one-token kernel)
 GEMM_I8_SHAPES = [(16384, 4096, 16), (4096, 16384, 16), (4096, 4096, 8), (4608, 4096, 5), (256, 4096, 16),
                   (33, 768, 3), (1000, 1280, 17), (3, 256, 40), (7, 65280, 3), (4096, 12288, 2),
-                  (300, 4352, 33), (16384, 4096, 1), (16384, 4096, 32)]
+                  (300, 4352, 33), (16384, 4096, 1), (16384, 4096, 32),
+                  # 2 to 4 tokens on the one-pass int8 matvec (1, 2 and 4 chunks,
+                  # partial last chunks, ragged rows, 16384x4096 at 3 on its 24 MiB
+                  # cap); 16384x4096 at 4 and 4096x16384 at 3 past it
+                  (4096, 4096, 2), (4096, 4096, 4), (16384, 4096, 2), (4096, 16384, 2),
+                  (257, 4352, 2), (1001, 7936, 4), (16384, 4096, 3), (16384, 4096, 4), (4096, 16384, 3)]
 
 
 @pytest.mark.parametrize("N,K,M", GEMM_I8_SHAPES)
