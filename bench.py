@@ -391,6 +391,7 @@ CONFIGS = [  # (label, N, K, kind, seed): the single-call configurations, timed 
     ("batched q/o 4096x4096, 16 tokens per call (tq2_gemm)", 4096, 4096, "gemm16", 1007),
     ("batched down 4096x16384 int8, 16 tokens per call (tq2_gemm_i8q)", 4096, 16384, "gemm_i8q16", 1008),
     ("batched gate 16384x4096 int8, 16 tokens per call (tq2_gemm_i8q)", 16384, 4096, "gemm_i8q16", 1009),
+    ("batched down 4096x16384 int8, 2 tokens per call (tq2_gemm_i8q)", 4096, 16384, "gemm_i8q2", 1010),
     # the adjacent entry points, each a single call on its own shape
     ("next: fused q/k/v 4096+256+256 x 4096 fp16 (tq2_gemv_fused)", 4096, 4096, "qkv", 1006),
     ("next: fused q/k/v 4096+256+256 x 4096 int8 (tq2_gemv_i8_fused)", 4096, 4096, "qkv_i8", 1006),
@@ -411,7 +412,7 @@ WARM_SECONDS = 0.25
 REQUANT_S_OUT = 0.05
 CPU_TIMED_KINDS = ("f16", "f16_out", "gate_up", "i8", "i8q")
 GEMM_TOKENS = {"gemm16": 16, "gemm1": 1, "gemm4": 4}
-GEMM_I8_TOKENS = {"gemm_i8q16": 16}  # tq2_gemm_i8q: pre-quantized int8 tokens
+GEMM_I8_TOKENS = {"gemm_i8q16": 16, "gemm_i8q2": 2}  # tq2_gemm_i8q: pre-quantized int8 tokens
 
 
 def config_bytes(kind, N, K, rows):
