@@ -876,21 +876,29 @@ def test_graph_capture_replay(tq2):
 
 def test_side_stream(tq2):
     """Calls on a non-default stream (passed explicitly) give the same bits as
-    on the default stream."""
+    on the default stream (the matvec, the batched fp16 and int8 calls)."""
     N, K, M = 4096, 4096, 3
     _, c, s, x = _packed(2400, N, K)
     dc, ds, xd = _to_dev(c, s, x)
     X = torch.stack([xd, xd.flip(0), xd * 0.5]).contiguous()
+    XQ3 = tq2.tq2_quantize_i8(X, 0.05)   # 3 tokens: the one-pass int8 matvec
+    XQ16 = tq2.tq2_quantize_i8(torch.cat([X] * 6)[:16].contiguous(), 0.05)  # the int8 matrix cores
     y0 = tq2.tq2_gemv(dc, ds, xd)
     Y0 = tq2.tq2_gemm(dc, ds, X)
+    Q0, Q16 = tq2.tq2_gemm_i8q(dc, ds, XQ3, 0.05), tq2.tq2_gemm_i8q(dc, ds, XQ16, 0.05)
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
     y1 = torch.empty_like(y0)
     Y1 = torch.empty_like(Y0)
+    Q1, Q17 = torch.empty_like(Q0), torch.empty_like(Q16)
     ws = torch.empty(max(256, tq2.tq2_gemm_workspace_bytes(N, K, M)), dtype=torch.uint8, device=DEV)
+    wsq = torch.empty(max(256, tq2.tq2_gemm_i8q_workspace_bytes(N, K, 16)), dtype=torch.uint8, device=DEV)
     tq2.tq2_gemv(dc, ds, xd, y=y1, stream=st)
     tq2.tq2_gemm(dc, ds, X, y=Y1, ws=ws, stream=st)
+    tq2.tq2_gemm_i8q(dc, ds, XQ3, 0.05, y=Q1, stream=st)
+    tq2.tq2_gemm_i8q(dc, ds, XQ16, 0.05, y=Q17, ws=wsq, stream=st)
     st.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
     assert torch.equal(Y0, Y1)
+    assert torch.equal(Q0, Q1) and torch.equal(Q16, Q17)
