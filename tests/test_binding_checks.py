@@ -113,3 +113,13 @@ def test_gemm_checked(tq2):
     _raises("x must be a", tq2.tq2_gemm, c, s, torch.zeros((3, K + 256), dtype=torch.float16))
     _raises("x must have dtype", tq2.tq2_gemm, c, s, X.float())
     _raises(f"y must hold {3 * N} elements", tq2.tq2_gemm, c, s, X, y=torch.zeros(3 * N - 1))
+
+
+def test_gemm_i8q_checked(tq2):
+    c, s = _w()
+    XQ = torch.zeros((3, K), dtype=torch.int8)
+    _raises("x_q must be a", tq2.tq2_gemm_i8q, c, s, torch.zeros((3, K + 256), dtype=torch.int8), 0.1)
+    _raises("x_q must have dtype", tq2.tq2_gemm_i8q, c, s, XQ.to(torch.uint8), 0.1)
+    _raises("x_q must have dtype", tq2.tq2_gemm_i8q, c, s, XQ.half(), 0.1)
+    _raises(f"y must hold {3 * N} elements", tq2.tq2_gemm_i8q, c, s, XQ, 0.1, y=torch.zeros(3 * N - 1))
+    _raises("y must have dtype", tq2.tq2_gemm_i8q, c, s, XQ, 0.1, y=torch.zeros(3 * N, dtype=torch.float16))
